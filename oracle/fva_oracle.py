@@ -1,0 +1,303 @@
+"""CPU oracle for adaptive block-sparse video attention (FVAttn's routing
+frontend and block-sparse attention).  TEST INFRASTRUCTURE ONLY.
+
+This module is the parity reference.  Only the tests, the smoke check and the
+benchmark's CPU-baseline leg may import it; the product path never does.  It
+shares no code with the HIP library: it is written directly from the FVAttn
+pages (papers.paperslantern.ai/papers/2607.16190) in plain numpy, float64
+unless a step's interface fixes another precision, with no blocking, fusion or
+reordering beyond what each step's definition states.
+
+Steps and the passages they follow (all on the FVAttn page):
+  block_order / reorder / unreorder  section 3.1, video-aware block organization
+                                     (reading: raster order over clipped tiles,
+                                     raster order inside a tile, tail padding)
+  pool                               section 3.1, block similarities from pooled Q/K
+  block_scores                       section 2 (importance score per head, q-block,
+                                     k-block) and section 3.1 (pooled Q/K)
+  route                              section 2 (Top-p: smallest set whose cumulative
+                                     normalized importance reaches p; Top-k floor)
+                                     and section 3.1 (Top-p CDF threshold, Top-k floor)
+  head_workload                      section 2 (realized per-head workload = number
+                                     of selected block pairs)
+  sasa_topup                         section 3.3 (extra budget spent in the
+                                     importance order produced by routing), one-GPU
+                                     per-head form
+  heaviest_first                     section 3.2 (load balancing on realized
+                                     workloads), one-GPU work-queue form
+  sparse_attention                   section 2 (only selected query-key block pairs
+                                     are evaluated)
+
+Every function here is pinned by tests against closed forms, brute force on
+tiny inputs, or a library routine for a special case (dense attention).
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# Video-aware block organization (section 3.1)
+# --------------------------------------------------------------------------
+
+def block_order(T: int, H: int, W: int, bt: int, bh: int, bw: int) -> np.ndarray:
+    """Reordered position r -> source token index, length N = T*H*W.
+
+    Tiles of bt x bh x bw tokens are visited in raster order (tile t, then tile
+    row, then tile column); tiles at the grid edge are clipped.  Inside a tile
+    the tokens are visited in raster order (t, y, x).  Source token index of
+    (t, y, x) is (t*H + y)*W + x.
+    """
+    out: List[np.ndarray] = []
+    for t0 in range(0, T, bt):
+        for y0 in range(0, H, bh):
+            for x0 in range(0, W, bw):
+                ts = np.arange(t0, min(t0 + bt, T))
+                ys = np.arange(y0, min(y0 + bh, H))
+                xs = np.arange(x0, min(x0 + bw, W))
+                tok = (ts[:, None, None] * H + ys[None, :, None]) * W + xs[None, None, :]
+                out.append(tok.reshape(-1))
+    order = np.concatenate(out).astype(np.int64)
+    assert order.shape[0] == T * H * W
+    return order
+
+
+def sizes(T, H, W, bt, bh, bw) -> Tuple[int, int, int, int]:
+    """(N, BLK, nB, Npad): tokens, tokens per block, blocks, padded length."""
+    N = T * H * W
+    BLK = bt * bh * bw
+    nB = -(-N // BLK)
+    return N, BLK, nB, nB * BLK
+
+
+def reorder(x: np.ndarray, grid: Sequence[int], block: Sequence[int]) -> np.ndarray:
+    """[B, N, Hh, d] -> [B, Hh, Npad, d] in block order, pad rows zero.
+    Pure data movement: the dtype is kept."""
+    N, BLK, nB, Npad = sizes(*grid, *block)
+    B, n, Hh, d = x.shape
+    assert n == N
+    order = block_order(*grid, *block)
+    y = np.zeros((B, Hh, Npad, d), dtype=x.dtype)
+    y[:, :, :N, :] = np.transpose(x[:, order, :, :], (0, 2, 1, 3))
+    return y
+
+
+def unreorder(y: np.ndarray, grid: Sequence[int], block: Sequence[int]) -> np.ndarray:
+    """[B, Hh, Npad, d] -> [B, N, Hh, d]; padded rows are dropped."""
+    N, BLK, nB, Npad = sizes(*grid, *block)
+    B, Hh, npad, d = y.shape
+    assert npad == Npad
+    order = block_order(*grid, *block)
+    x = np.empty((B, N, Hh, d), dtype=y.dtype)
+    x[:, order, :, :] = np.transpose(y[:, :, :N, :], (0, 2, 1, 3))
+    return x
+
+
+# --------------------------------------------------------------------------
+# Routing frontend (sections 2 and 3.1)
+# --------------------------------------------------------------------------
+
+def pool(xr: np.ndarray, N: int, BLK: int) -> np.ndarray:
+    """Mean of each block's real tokens: [B, Hh, Npad, d] -> [B, Hh, nB, d] f64.
+    The last block may be partial; its mean is over its real tokens only."""
+    B, Hh, Npad, d = xr.shape
+    nB = Npad // BLK
+    out = np.empty((B, Hh, nB, d), dtype=np.float64)
+    for b in range(nB):
+        lo, hi = b * BLK, min((b + 1) * BLK, N)
+        out[:, :, b, :] = xr[:, :, lo:hi, :].astype(np.float64).sum(axis=2) / (hi - lo)
+    return out
+
+
+def block_scores(qbar: np.ndarray, kbar: np.ndarray, scale: float) -> np.ndarray:
+    """s[b,h,i,j] = (qbar_i . kbar_j) * scale, float64 [B, Hh, nB, nB]."""
+    return np.matmul(qbar, np.swapaxes(kbar, -1, -2)) * scale
+
+
+def scores_f32(S: np.ndarray) -> np.ndarray:
+    """The routing interface carries scores as IEEE float32 (round to nearest)."""
+    return S.astype(np.float32)
+
+
+def route_order(S32: np.ndarray) -> np.ndarray:
+    """Key-block importance order per row: score descending, ties by key-block
+    index ascending.  -0 and +0 compare equal.  NaN scores are rejected."""
+    S32 = np.asarray(S32, dtype=np.float32)
+    if np.isnan(S32).any():
+        raise ValueError("NaN block score")
+    nB = S32.shape[-1]
+    flat = S32.reshape(-1, nB)
+    j = np.broadcast_to(np.arange(nB), flat.shape)
+    # lexsort: last key is primary -> primary = -score (desc), secondary = j (asc)
+    neg = -(flat.astype(np.float64))
+    order = np.lexsort((j, neg), axis=-1)
+    return order.reshape(S32.shape)
+
+
+def route(S32: np.ndarray, top_p: float, topk: int):
+    """Top-p CDF cut with a Top-k floor, per (batch, head, query block) row.
+
+    S32: float32 [..., nB, nB] block scores.  top_p is taken at its float32
+    value.  For each row, key blocks are put in importance order; the softmax of
+    the row's scores is accumulated in that order in float64
+    (e_j = exp(s_j - max), C_n = e_1 + ... + e_n in sequence, Z = C_nB) and the
+    Top-p set is the shortest prefix with C_n >= p*Z (all blocks when p >= 1,
+    none when p <= 0).  The Top-k floor extends it to at least k blocks; the
+    union of the two prefixes is the longer one.
+
+    Returns (mask bool [..., nB, nB], counts int64 [..., nB], margin f64 [..., nB])
+    where margin is min(|C_n* - pZ|, |C_(n*-1) - pZ|) / Z, the distance of the
+    cut from flipping (inf where the cut was not decided by the CDF).
+    """
+    S32 = np.asarray(S32, dtype=np.float32)
+    nB = S32.shape[-1]
+    rows = S32.reshape(-1, nB)
+    order = route_order(rows)
+    p = float(np.float32(top_p))
+    R = rows.shape[0]
+    counts = np.empty(R, dtype=np.int64)
+    margin = np.full(R, np.inf)
+    mask = np.zeros((R, nB), dtype=bool)
+    for r in range(R):
+        s = rows[r, order[r]].astype(np.float64)
+        if p >= 1.0:
+            nstar = nB
+        elif p <= 0.0:
+            nstar = 0
+        else:
+            e = np.exp(s - s[0])
+            C = np.cumsum(e)               # sequential, importance order
+            Z = C[-1]
+            target = p * Z
+            nstar = int(np.argmax(C >= target)) + 1
+            m = abs(C[nstar - 1] - target)
+            if nstar >= 2:
+                m = min(m, abs(C[nstar - 2] - target))
+            margin[r] = m / Z
+        n = min(nB, max(nstar, int(topk)))
+        counts[r] = n
+        mask[r, order[r, :n]] = True
+    return (mask.reshape(S32.shape), counts.reshape(S32.shape[:-1]),
+            margin.reshape(S32.shape[:-1]))
+
+
+def head_workload(mask: np.ndarray) -> np.ndarray:
+    """W_h: number of selected (q-block, k-block) pairs per (batch, head)."""
+    return mask.reshape(mask.shape[0], mask.shape[1], -1).sum(axis=-1).astype(np.int64)
+
+
+def sasa_topup(S32: np.ndarray, mask: np.ndarray, budget: int) -> np.ndarray:
+    """One-GPU form of slack-aware augmentation: per head, when its workload
+    W_h is below `budget` pairs, add the budget - W_h unselected pairs with the
+    highest scores (ties: query block ascending, then key block ascending).
+    Heads at or above the budget are unchanged.  budget <= 0 disables it."""
+    out = mask.copy()
+    if budget <= 0:
+        return out
+    B, Hh, nB, _ = mask.shape
+    ii, jj = np.meshgrid(np.arange(nB), np.arange(nB), indexing="ij")
+    for b in range(B):
+        for h in range(Hh):
+            m = out[b, h]
+            need = budget - int(m.sum())
+            if need <= 0:
+                continue
+            free = ~m
+            s = S32[b, h][free].astype(np.float64)
+            fi, fj = ii[free], jj[free]
+            pick = np.lexsort((fj, fi, -s))[:need]
+            m[fi[pick], fj[pick]] = True
+    return out
+
+
+def heaviest_first(counts: np.ndarray) -> np.ndarray:
+    """Work items (b*Hh + h)*nB + i ordered by row count descending, ties by
+    item id ascending."""
+    flat = counts.reshape(-1)
+    ids = np.arange(flat.shape[0])
+    return np.array(sorted(ids.tolist(), key=lambda t: (-int(flat[t]), t)), dtype=np.int64)
+
+
+# --------------------------------------------------------------------------
+# Block-sparse attention (section 2: only selected block pairs are evaluated)
+# --------------------------------------------------------------------------
+
+def sparse_attention_block(qr, kr, vr, mask_row, N: int, BLK: int, scale: float,
+                           qb: int) -> np.ndarray:
+    """Output rows of query block qb for one (batch, head).
+
+    qr, kr, vr: [Npad, d] arrays of that head in block order.  mask_row: bool
+    [nB] selected key blocks.  Keys are the real tokens (position < N) of the
+    selected blocks in ascending block order; two-pass softmax over them in
+    float64.  Returns [n_real_rows, d] float64; zeros when nothing is selected.
+    """
+    lo, hi = qb * BLK, min((qb + 1) * BLK, N)
+    q = qr[lo:hi].astype(np.float64)
+    sel = np.nonzero(mask_row)[0]
+    if sel.size == 0:
+        return np.zeros((hi - lo, qr.shape[1]), dtype=np.float64)
+    keys = np.concatenate([np.arange(j * BLK, min((j + 1) * BLK, N)) for j in sel])
+    k = kr[keys].astype(np.float64)
+    v = vr[keys].astype(np.float64)
+    logits = (q @ k.T) * scale
+    m = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - m)
+    return (e @ v) / e.sum(axis=1, keepdims=True)
+
+
+def sparse_attention(qr, kr, vr, mask, N: int, BLK: int, scale: float,
+                     items: Optional[Iterable[Tuple[int, int, int]]] = None):
+    """Block-sparse attention over reordered tensors [B, Hh, Npad, d].
+
+    With items=None returns the full [B, Hh, Npad, d] float64 output (pad rows
+    zero).  With a list of (b, h, qb) returns {item: [rows, d] float64}."""
+    B, Hh, Npad, d = qr.shape
+    nB = Npad // BLK
+    if items is None:
+        out = np.zeros((B, Hh, Npad, d), dtype=np.float64)
+        for b in range(B):
+            for h in range(Hh):
+                for i in range(nB):
+                    lo, hi = i * BLK, min((i + 1) * BLK, N)
+                    out[b, h, lo:hi] = sparse_attention_block(
+                        qr[b, h], kr[b, h], vr[b, h], mask[b, h, i], N, BLK, scale, i)
+        return out
+    res = {}
+    for (b, h, i) in items:
+        res[(b, h, i)] = sparse_attention_block(qr[b, h], kr[b, h], vr[b, h],
+                                                mask[b, h, i], N, BLK, scale, i)
+    return res
+
+
+# --------------------------------------------------------------------------
+# Whole path
+# --------------------------------------------------------------------------
+
+def route_path(qr, kr, N, BLK, scale, top_p, topk, aug_budget=0) -> Dict[str, np.ndarray]:
+    """pool -> scores -> float32 -> Top-p/Top-k route -> optional top-up ->
+    workloads and heaviest-first queue."""
+    qbar = pool(qr, N, BLK)
+    kbar = pool(kr, N, BLK)
+    S = block_scores(qbar, kbar, scale)
+    S32 = scores_f32(S)
+    mask, counts, margin = route(S32, top_p, topk)
+    mask_aug = sasa_topup(S32, mask, aug_budget)
+    counts_aug = mask_aug.sum(axis=-1).astype(np.int64)
+    return dict(qbar=qbar, kbar=kbar, scores=S, scores32=S32, mask_routed=mask,
+                counts_routed=counts, margin=margin, mask=mask_aug, counts=counts_aug,
+                head_count=head_workload(mask_aug), queue=heaviest_first(counts_aug))
+
+
+def forward(q, k, v, grid, block, top_p, topk, aug_budget=0, scale=None):
+    """Full path on [B, N, Hh, d] inputs; returns (O [B, N, Hh, d] f64, route dict)."""
+    N, BLK, nB, Npad = sizes(*grid, *block)
+    d = q.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    qr, kr, vr = (reorder(x, grid, block) for x in (q, k, v))
+    r = route_path(qr, kr, N, BLK, scale, top_p, topk, aug_budget)
+    orr = sparse_attention(qr, kr, vr, r["mask"], N, BLK, scale)
+    return unreorder(orr, grid, block), r

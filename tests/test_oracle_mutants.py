@@ -1,0 +1,79 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check that
+some pin in test_oracle.py catches each one."""
+
+import os
+import types
+
+import pytest
+
+import test_oracle as T
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "fva_oracle.py")
+
+MUTANTS = [
+    ("tile inner order column-major",
+     "tok = (ts[:, None, None] * H + ys[None, :, None]) * W + xs[None, None, :]",
+     "tok = np.transpose((ts[:, None, None] * H + ys[None, :, None]) * W + xs[None, None, :], (0, 2, 1))",
+     ["test_block_order_golden"]),
+    ("unreorder ignores the permutation",
+     "x[:, order, :, :] = np.transpose(y[:, :, :N, :], (0, 2, 1, 3))",
+     "x[:, :, :, :] = np.transpose(y[:, :, :N, :], (0, 2, 1, 3))",
+     ["test_reorder_roundtrip_and_padding"]),
+    ("pool divides by the block size",
+     "sum(axis=2) / (hi - lo)", "sum(axis=2) / BLK",
+     ["test_pool_partial_last_block_uses_real_tokens_only"]),
+    ("scores transposed",
+     "np.matmul(qbar, np.swapaxes(kbar, -1, -2)) * scale",
+     "np.matmul(kbar, np.swapaxes(qbar, -1, -2)) * scale",
+     ["test_scores_rank_one_closed_form"]),
+    ("scores miss the scale",
+     "np.matmul(qbar, np.swapaxes(kbar, -1, -2)) * scale",
+     "np.matmul(qbar, np.swapaxes(kbar, -1, -2))",
+     ["test_scores_rank_one_closed_form"]),
+    ("cut uses > instead of >=", "nstar = int(np.argmax(C >= target)) + 1",
+     "nstar = int(np.argmax(C > target)) + 1", ["test_route_worked_examples"]),
+    ("ties broken by descending index",
+     "j = np.broadcast_to(np.arange(nB), flat.shape)",
+     "j = np.broadcast_to(np.arange(nB)[::-1], flat.shape)",
+     ["test_route_worked_examples"]),
+    ("floor intersected instead of unioned",
+     "n = min(nB, max(nstar, int(topk)))", "n = min(nB, min(nstar, int(topk)))",
+     ["test_route_worked_examples", "test_route_bruteforce_minimal_prefix"]),
+    ("cumulative sum in index order, not importance order",
+     "e = np.exp(s - s[0])", "e = np.exp(rows[r].astype(np.float64) - s[0])",
+     ["test_route_worked_examples"]),
+    ("top-up ties j before i", "pick = np.lexsort((fj, fi, -s))[:need]",
+     "pick = np.lexsort((fi, fj, -s))[:need]", ["test_sasa_topup_bruteforce"]),
+    ("top-up takes the lowest scores", "pick = np.lexsort((fj, fi, -s))[:need]",
+     "pick = np.lexsort((fj, fi, s))[:need]", ["test_sasa_topup_bruteforce"]),
+    ("attention keeps padded keys",
+     "keys = np.concatenate([np.arange(j * BLK, min((j + 1) * BLK, N)) for j in sel])",
+     "keys = np.concatenate([np.arange(j * BLK, (j + 1) * BLK) for j in sel])",
+     ["test_zero_queries_average_selected_real_values"]),
+    ("attention drops the scale", "logits = (q @ k.T) * scale", "logits = (q @ k.T)",
+     ["test_sparse_output_equals_dense_on_selected_keys_only"]),
+    ("queue lightest-first", "key=lambda t: (-int(flat[t]), t)",
+     "key=lambda t: (int(flat[t]), t)", ["test_heaviest_first_order"]),
+]
+
+
+def _mutant_module(old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, old
+    mod = types.ModuleType("fva_oracle_mutant")
+    mod.__dict__["__file__"] = SRC
+    exec(compile(src.replace(old, new, 1), SRC + "<mutant>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name,old,new,catchers", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pin_catches_mutant(name, old, new, catchers, monkeypatch):
+    monkeypatch.setattr(T, "O", _mutant_module(old, new))
+    caught = []
+    for t in catchers:
+        try:
+            getattr(T, t)()
+        except Exception:
+            caught.append(t)
+    assert caught, f"no pin caught mutant: {name}"
