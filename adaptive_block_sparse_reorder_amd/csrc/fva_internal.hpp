@@ -1,0 +1,84 @@
+// Internal declarations shared by the libfva translation units (HIP, gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fva.h"
+
+namespace fva {
+
+// ---------------------------------------------------------------- host side
+
+// Records a thread-local error message and returns `s`.
+fva_status fail(fva_status s, const char* fmt, ...);
+// Maps a HIP error to FVA_ERR_HIP with a message naming `what`.
+fva_status hip_fail(hipError_t e, const char* what);
+
+struct Problem {
+  int32_t B, Hh, d;
+  int32_t T, H, W, bt, bh, bw;
+  int64_t N, Npad;
+  int32_t BLK, nB, words;
+  int64_t rows;  // B*Hh*nB
+};
+
+// Validates grid/shape and fills `p`.  Returns FVA_OK or an error status.
+fva_status make_problem(const fva_grid* g, int32_t B, int32_t Hh, int32_t d, Problem* p);
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+// Route workspace layout (byte offsets, 256-aligned).
+struct RouteWs {
+  size_t flags_off;     // uint32 status word
+  size_t qbar_off;      // float [rows, d]
+  size_t kbar_off;      // float [rows, d]
+  size_t thresh_off;    // uint64 [B*Hh] top-up threshold keys
+  size_t total;
+};
+RouteWs route_ws_layout(const Problem& p);
+constexpr size_t kAttnWsBytes = 256;
+
+// Kernel launchers (each returns FVA_OK or FVA_ERR_HIP).
+fva_status launch_reorder(const Problem& p, const void* src, void* dst, const int64_t st[3],
+                          int direction, int layout, hipStream_t s);
+fva_status launch_route(const Problem& p, const void* qr, const void* kr,
+                        const fva_route_params& prm, float scale, const fva_mask& m,
+                        char* ws, int flags, hipStream_t s);
+fva_status launch_attn(const Problem& p, const void* qr, const void* kr, const void* vt,
+                       void* out, const fva_mask* m, float scale, int flags, void* ws,
+                       void* trace, bool dense, hipStream_t s);
+
+// ---------------------------------------------------------------- device side
+
+// Reordered position r (< N) -> source token index, for raster order over
+// clipped tiles and raster order inside a tile.  Closed form: every tile frame
+// slab (all tiles with the same tile-t index) covers whole frames, and every
+// tile row inside a slab covers whole rows, so the tile containing r follows
+// from three divisions.
+struct BlockOrder {
+  int32_t T, H, W, bt, bh, bw;
+  __device__ __forceinline__ int64_t src_token(int64_t r) const {
+    const int64_t HW = (int64_t)H * W;
+    const int64_t slab = (int64_t)bt * HW;
+    const int32_t tt = (int32_t)(r / slab);
+    int64_t r1 = r - (int64_t)tt * slab;
+    const int32_t st = min(bt, T - tt * bt);
+    const int64_t rowband = (int64_t)st * bh * W;
+    const int32_t ty = (int32_t)(r1 / rowband);
+    int64_t r2 = r1 - (int64_t)ty * rowband;
+    const int32_t sy = min(bh, H - ty * bh);
+    const int32_t tilesz = st * sy * bw;
+    const int32_t tx = (int32_t)(r2 / tilesz);
+    const int32_t r3 = (int32_t)(r2 - (int64_t)tx * tilesz);
+    const int32_t sx = min(bw, W - tx * bw);
+    const int32_t t = r3 / (sy * sx);
+    const int32_t rem = r3 - t * (sy * sx);
+    const int32_t y = rem / sx;
+    const int32_t x = rem - y * sx;
+    return ((int64_t)(tt * bt + t) * H + (ty * bh + y)) * W + (tx * bw + x);
+  }
+};
+
+}  // namespace fva

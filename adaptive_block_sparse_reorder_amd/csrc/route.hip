@@ -1,0 +1,492 @@
+// Sparse-routing frontend (FVAttn page, sections 2 and 3.1; top-up: section
+// 3.3): block mean-pooling of Q and K, pooled block scores, the Top-p CDF cut
+// with a Top-k floor, mask materialization (bitmask, per-row counts, ascending
+// column lists, per-head workload), the optional per-head top-up, and the
+// heaviest-first work queue.
+#include "fva_internal.hpp"
+
+namespace fva {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Monotone map float32 -> uint32 (larger float -> larger key); -0 == +0.
+__device__ __forceinline__ uint32_t order_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if ((u & 0x7fffffffu) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float order_key_inv(uint32_t k) {
+  const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+__global__ void zero_route_state(int32_t* head_count, int nheads, uint32_t* flags) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nheads) head_count[i] = 0;
+  if (i == 0) *flags = 0u;
+}
+
+// ------------------------------------------------------------------ pooling
+// grid (nB, B*Hh, 2 [q|k]); 256 threads; thread = (row group, 16-byte chunk).
+template <int D>
+__global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ qr,
+                                                   const uint16_t* __restrict__ kr,
+                                                   float* __restrict__ qbar,
+                                                   float* __restrict__ kbar, int64_t N,
+                                                   int64_t Npad, int BLK, int nB) {
+  constexpr int CPR = D / 8;           // chunks per row
+  constexpr int RG = 256 / CPR;        // row groups
+  constexpr int WRG = 64 / CPR;        // row groups per wave
+  __shared__ float part[4][D];
+  const int blk = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const uint16_t* x = (blockIdx.z == 0 ? qr : kr) + (bh * Npad + (int64_t)blk * BLK) * D;
+  float* out = (blockIdx.z == 0 ? qbar : kbar) + (bh * nB + blk) * D;
+  const int nreal = (int)min((int64_t)BLK, N - (int64_t)blk * BLK);
+  const int c = threadIdx.x % CPR;
+  const int rg = threadIdx.x / CPR;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r = rg; r < nreal; r += RG) {
+    const u32x4 v = *(const u32x4*)(x + (int64_t)r * D + c * 8);
+    acc[0] += bf16_lo(v.x); acc[1] += bf16_hi(v.x);
+    acc[2] += bf16_lo(v.y); acc[3] += bf16_hi(v.y);
+    acc[4] += bf16_lo(v.z); acc[5] += bf16_hi(v.z);
+    acc[6] += bf16_lo(v.w); acc[7] += bf16_hi(v.w);
+  }
+  // reduce the row groups of this wave (lanes that share a chunk)
+#pragma unroll
+  for (int off = CPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
+  }
+  const int wave = threadIdx.x / 64;
+  if ((threadIdx.x % 64) < CPR) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[wave][c * 8 + e] = acc[e];
+  }
+  (void)WRG;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const float s = (part[0][threadIdx.x] + part[1][threadIdx.x]) +
+                    (part[2][threadIdx.x] + part[3][threadIdx.x]);
+    out[threadIdx.x] = s / (float)nreal;
+  }
+}
+
+// ------------------------------------------------------------------ scores
+// S[bh, i, j] = scale * sum_c qbar[bh, i, c] * kbar[bh, j, c]; 64x64 tiles.
+template <int D>
+__global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qbar,
+                                                    const float* __restrict__ kbar,
+                                                    float* __restrict__ S, int nB, float scale) {
+  constexpr int KC = 32;
+  __shared__ float qs[64][KC + 1];
+  __shared__ float ks[64][KC + 1];
+  const int64_t bh = blockIdx.z;
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  const float* qb = qbar + bh * nB * D;
+  const float* kb = kbar + bh * nB * D;
+  float acc[4][4] = {};
+  for (int c0 = 0; c0 < D; c0 += KC) {
+    for (int L = threadIdx.x; L < 64 * KC; L += 256) {
+      const int r = L / KC, c = L % KC;
+      qs[r][c] = (i0 + r < nB) ? qb[(int64_t)(i0 + r) * D + c0 + c] : 0.f;
+      ks[r][c] = (j0 + r < nB) ? kb[(int64_t)(j0 + r) * D + c0 + c] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int c = 0; c < KC; ++c) {
+      float a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { a[u] = qs[ty + 16 * u][c]; b[u] = ks[tx + 16 * u][c]; }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(a[u], b[v], acc[u][v]);
+    }
+    __syncthreads();
+  }
+  float* Sb = S + bh * (int64_t)nB * nB;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = i0 + ty + 16 * u, j = j0 + tx + 16 * v;
+      if (i < nB && j < nB) Sb[(int64_t)i * nB + j] = acc[u][v] * scale;
+    }
+}
+
+// ------------------------------------------------------------------ block helpers
+
+// Inclusive scan of doubles across a 256-thread block (4 waves).
+__device__ double block_incl_scan_f64(double v, double* wsum) {
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  double base = 0.0;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  __syncthreads();
+  return base + v;
+}
+
+template <int NT>
+__device__ int block_sum_i32(int v, int* red) {
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  int t = 0;
+  for (int w = 0; w < NT / 64; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+// Bitonic sort (ascending) of P keys in LDS by NT threads.
+template <typename K, int NT>
+__device__ void bitonic_sort(K* keys, int P) {
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int q = threadIdx.x; q < P / 2; q += NT) {
+        const int i = 2 * j * (q / j) + (q % j);
+        const int l = i + j;
+        const K a = keys[i], b = keys[l];
+        const bool up = (i & k) == 0;
+        if ((a > b) == up) { keys[i] = b; keys[l] = a; }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Writes bitmask words, and the ascending column list, of one row from the
+// LDS bitmask `bits` (words entries).  Returns nothing; col_idx gets popcount
+// entries.  Must be called by all threads of the block.
+template <int NT>
+__device__ void emit_row(const uint32_t* bits, int words, uint32_t* bm_out, int16_t* col_out,
+                         int* wpre) {
+  if (threadIdx.x < words) {
+    bm_out[threadIdx.x] = bits[threadIdx.x];
+    int pre = 0;
+    for (int w = 0; w < (int)threadIdx.x; ++w) pre += __popc(bits[w]);
+    wpre[threadIdx.x] = pre;
+  }
+  __syncthreads();
+  if (threadIdx.x < words) {
+    uint32_t m = bits[threadIdx.x];
+    int pos = wpre[threadIdx.x];
+    while (m) {
+      const int bit = __ffs(m) - 1;
+      m &= m - 1u;
+      col_out[pos++] = (int16_t)(threadIdx.x * 32 + bit);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ route
+// One 256-thread workgroup per row; P = padded sort length (power of two).
+constexpr int kRouteThreads = 256;
+constexpr int kMaxNB = 2048;
+
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(
+    const float* __restrict__ S, int nB, int words, int P, float top_p, int topk,
+    uint32_t* __restrict__ bitmask, int32_t* __restrict__ row_count,
+    int16_t* __restrict__ col_idx, int32_t* __restrict__ head_count, uint32_t* flags) {
+  __shared__ uint64_t keys[kMaxNB];
+  __shared__ uint32_t bits[kMaxNB / 32];
+  __shared__ double wsum[4];
+  __shared__ int red[4];
+  __shared__ int wpre[kMaxNB / 32];
+  const int64_t row = blockIdx.x;
+  const int64_t bh = row / nB;
+  const float* s = S + row * nB;
+  int nan_seen = 0;
+  for (int j = threadIdx.x; j < P; j += kRouteThreads) {
+    uint64_t key = ~0ull;
+    if (j < nB) {
+      const float v = s[j];
+      nan_seen |= (v != v);
+      key = ((uint64_t)(~order_key(v)) << 32) | (uint32_t)j;
+    }
+    keys[j] = key;
+  }
+  for (int w = threadIdx.x; w < words; w += kRouteThreads) bits[w] = 0u;
+  if (nan_seen) atomicOr(flags, 1u);
+  __syncthreads();
+  bitonic_sort<uint64_t, kRouteThreads>(keys, P);
+
+  // float64 softmax mass accumulated in importance order
+  const int ept = P / kRouteThreads;           // consecutive sorted slots per thread
+  const int t0 = threadIdx.x * ept;
+  int nstar;
+  if (top_p >= 1.0f) {
+    nstar = nB;
+  } else if (top_p <= 0.0f) {
+    nstar = 0;
+  } else {
+    const double m = (double)order_key_inv(~(uint32_t)(keys[0] >> 32));
+    double e[8];
+    double local = 0.0;
+    for (int u = 0; u < ept; ++u) {
+      const int t = t0 + u;
+      double v = 0.0;
+      if (t < nB) v = exp((double)order_key_inv(~(uint32_t)(keys[t] >> 32)) - m);
+      e[u] = v;
+      local += v;
+    }
+    const double incl = block_incl_scan_f64(local, wsum);
+    __shared__ double Zs;
+    if (threadIdx.x == kRouteThreads - 1) Zs = incl;
+    __syncthreads();
+    const double target = (double)top_p * Zs;
+    double c = incl - local;
+    int below = 0;
+    for (int u = 0; u < ept; ++u) {
+      c += e[u];
+      if (t0 + u < nB && c < target) ++below;
+    }
+    nstar = min(nB, block_sum_i32<kRouteThreads>(below, red) + 1);
+  }
+  const int n = min(nB, max(nstar, topk));
+  for (int u = 0; u < ept; ++u) {
+    const int t = t0 + u;
+    if (t < n) {
+      const uint32_t j = (uint32_t)keys[t];
+      atomicOr(&bits[j >> 5], 1u << (j & 31));
+    }
+  }
+  __syncthreads();
+  emit_row<kRouteThreads>(bits, words, bitmask + row * words, col_idx + row * nB, wpre);
+  if (threadIdx.x == 0) {
+    row_count[row] = n;
+    atomicAdd(&head_count[bh], n);
+  }
+}
+
+// ------------------------------------------------------------------ top-up
+// Priority key of pair (i, j) with score s: smaller = higher priority
+// (score descending, then i ascending, then j ascending).  62 bits.
+__device__ __forceinline__ uint64_t pair_key(float s, int i, int j) {
+  return ((uint64_t)(~order_key(s)) << 30) | ((uint64_t)i << 15) | (uint64_t)j;
+}
+
+constexpr int kSelThreads = 1024;
+
+// One workgroup per head: exact radix select (8-bit digits, 8 passes) of the
+// need-th smallest priority key among unselected pairs.  thresh[bh] is an
+// exclusive bound: pairs with key < thresh are added; 0 means none.
+__global__ __launch_bounds__(kSelThreads) void topup_select_kernel(
+    const float* __restrict__ S, const uint32_t* __restrict__ bitmask,
+    const int32_t* __restrict__ head_count, int nB, int words, int64_t budget,
+    uint64_t* __restrict__ thresh) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint64_t s_prefix;
+  __shared__ int64_t s_need;
+  const int64_t bh = blockIdx.x;
+  const int64_t pairs = (int64_t)nB * nB;
+  const int64_t W = head_count[bh];
+  int64_t need = budget - W;
+  if (need <= 0) {
+    if (threadIdx.x == 0) thresh[bh] = 0ull;
+    return;
+  }
+  if (need >= pairs - W) {
+    if (threadIdx.x == 0) thresh[bh] = ~0ull;
+    return;
+  }
+  const float* Sh = S + bh * pairs;
+  const uint32_t* Bh = bitmask + bh * (int64_t)nB * words;
+  if (threadIdx.x == 0) { s_prefix = 0ull; s_need = need; }
+  __syncthreads();
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 54 - 8 * pass;       // digits at 54, 46, ..., 6, then 0 (6 bits)
+    const int sh = shift < 0 ? 0 : shift;
+    const int hishift = pass == 0 ? 64 : sh + (pass == 7 ? 6 : 8);
+    for (int b = threadIdx.x; b < 256; b += kSelThreads) hist[b] = 0u;
+    __syncthreads();
+    const uint64_t prefix = s_prefix;
+    for (int64_t q = threadIdx.x; q < pairs; q += kSelThreads) {
+      const int i = (int)(q / nB), j = (int)(q - (int64_t)i * nB);
+      if ((Bh[(int64_t)i * words + (j >> 5)] >> (j & 31)) & 1u) continue;
+      const uint64_t key = pair_key(Sh[q], i, j);
+      if (hishift < 64 && (key >> hishift) != prefix) continue;
+      const uint32_t digit = (uint32_t)((key >> sh) & (pass == 7 ? 63u : 255u));
+      atomicAdd(&hist[digit], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int64_t nd = s_need;
+      uint32_t d = 0;
+      for (; d < 256; ++d) {
+        if ((int64_t)hist[d] >= nd) break;
+        nd -= hist[d];
+      }
+      s_need = nd;
+      s_prefix = (prefix << (pass == 7 ? 6 : 8)) | d;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) thresh[bh] = s_prefix + 1ull;
+}
+
+// One workgroup per row of a topped-up head: add pairs below the threshold,
+// rewrite the row's bitmask, count and column list, and the head workload.
+__global__ __launch_bounds__(kRouteThreads) void topup_apply_kernel(
+    const float* __restrict__ S, int nB, int words, const uint64_t* __restrict__ thresh,
+    uint32_t* __restrict__ bitmask, int32_t* __restrict__ row_count,
+    int16_t* __restrict__ col_idx, int32_t* __restrict__ head_count) {
+  __shared__ uint32_t bits[kMaxNB / 32];
+  __shared__ int red[4];
+  __shared__ int wpre[kMaxNB / 32];
+  const int64_t row = blockIdx.x;
+  const int64_t bh = row / nB;
+  const int i = (int)(row - bh * nB);
+  const uint64_t th = thresh[bh];
+  if (th == 0ull) return;
+  uint32_t* bm = bitmask + row * words;
+  for (int w = threadIdx.x; w < words; w += kRouteThreads) bits[w] = bm[w];
+  __syncthreads();
+  int added = 0;
+  const float* s = S + row * nB;
+  for (int j = threadIdx.x; j < nB; j += kRouteThreads) {
+    const bool sel = (bits[j >> 5] >> (j & 31)) & 1u;
+    if (!sel && pair_key(s[j], i, j) < th) {
+      atomicOr(&bits[j >> 5], 1u << (j & 31));
+      ++added;
+    }
+  }
+  __syncthreads();
+  const int tot = block_sum_i32<kRouteThreads>(added, red);
+  if (tot == 0) return;
+  emit_row<kRouteThreads>(bits, words, bm, col_idx + row * nB, wpre);
+  if (threadIdx.x == 0) {
+    row_count[row] += tot;
+    atomicAdd(&head_count[bh], tot);
+  }
+}
+
+// ------------------------------------------------------------------ queue
+// One 1024-thread workgroup: stable counting sort of rows by count,
+// descending.  Rounds of 1024 rows are sorted in LDS by (count desc, row);
+// each row lands at the running offset of its count plus its rank in the run.
+constexpr int kQThreads = 1024;
+
+__global__ __launch_bounds__(kQThreads) void queue_kernel(const int32_t* __restrict__ row_count,
+                                                          int64_t rows, int nB,
+                                                          int32_t* __restrict__ queue) {
+  __shared__ int32_t off[kMaxNB + 2];
+  __shared__ uint32_t keys[kQThreads];
+  __shared__ int32_t start[kQThreads];
+  __shared__ int32_t wtot[kQThreads / 64];
+  const int nbins = nB + 1;
+  for (int c = threadIdx.x; c < nbins; c += kQThreads) off[c] = 0;
+  __syncthreads();
+  for (int64_t r = threadIdx.x; r < rows; r += kQThreads) atomicAdd(&off[row_count[r]], 1);
+  __syncthreads();
+  // exclusive scan in descending count order, sequential per wave chunk
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int c = nB; c >= 0; --c) {
+      const int h = off[c];
+      off[c] = run;
+      run += h;
+    }
+  }
+  __syncthreads();
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  for (int64_t base = 0; base < rows; base += kQThreads) {
+    const int64_t item = base + threadIdx.x;
+    keys[threadIdx.x] = item < rows
+                            ? ((uint32_t)(nB - row_count[item]) << 10) | (uint32_t)threadIdx.x
+                            : 0xffffffffu;
+    __syncthreads();
+    bitonic_sort<uint32_t, kQThreads>(keys, kQThreads);
+    const uint32_t k = keys[threadIdx.x];
+    const bool valid = k != 0xffffffffu;
+    const uint32_t grp = k >> 10;
+    const bool head = threadIdx.x == 0 || (keys[threadIdx.x - 1] >> 10) != grp;
+    // inclusive max-scan of run starts
+    int st = head ? (int)threadIdx.x : 0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(st, o, 64);
+      if (lane >= o) st = max(st, v);
+    }
+    if (lane == 63) wtot[wave] = st;
+    __syncthreads();
+    int carry = 0;
+    for (int w = 0; w < wave; ++w) carry = max(carry, wtot[w]);
+    st = max(st, carry);
+    start[threadIdx.x] = st;
+    __syncthreads();
+    if (valid) {
+      const int c = nB - (int)grp;
+      const int rank = (int)threadIdx.x - st;
+      queue[off[c] + rank] = (int32_t)(base + (k & 1023u));
+    }
+    __syncthreads();
+    if (valid) {
+      const bool tail = threadIdx.x == kQThreads - 1 || (keys[threadIdx.x + 1] >> 10) != grp;
+      if (tail) off[nB - (int)grp] += (int)threadIdx.x - st + 1;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+fva_status launch_route(const Problem& p, const void* qr, const void* kr,
+                        const fva_route_params& prm, float scale, const fva_mask& m,
+                        char* ws, int flags, hipStream_t s) {
+  const RouteWs L = route_ws_layout(p);
+  uint32_t* wflags = (uint32_t*)(ws + L.flags_off);
+  float* qbar = (float*)(ws + L.qbar_off);
+  float* kbar = (float*)(ws + L.kbar_off);
+  uint64_t* thresh = (uint64_t*)(ws + L.thresh_off);
+  const int nheads = p.B * p.Hh;
+  hipLaunchKernelGGL(zero_route_state, dim3((nheads + 255) / 256), dim3(256), 0, s,
+                     m.head_count, nheads, wflags);
+  if (!(flags & FVA_ROUTE_SCORES_IN)) {
+    dim3 pg(p.nB, nheads, 2);
+    if (p.d == 128)
+      hipLaunchKernelGGL(pool_kernel<128>, pg, dim3(256), 0, s, (const uint16_t*)qr,
+                         (const uint16_t*)kr, qbar, kbar, p.N, p.Npad, p.BLK, p.nB);
+    else
+      hipLaunchKernelGGL(pool_kernel<64>, pg, dim3(256), 0, s, (const uint16_t*)qr,
+                         (const uint16_t*)kr, qbar, kbar, p.N, p.Npad, p.BLK, p.nB);
+    dim3 sg((p.nB + 63) / 64, (p.nB + 63) / 64, nheads);
+    if (p.d == 128)
+      hipLaunchKernelGGL(score_kernel<128>, sg, dim3(256), 0, s, qbar, kbar, m.scores, p.nB,
+                         scale);
+    else
+      hipLaunchKernelGGL(score_kernel<64>, sg, dim3(256), 0, s, qbar, kbar, m.scores, p.nB,
+                         scale);
+  }
+  int P = 256;
+  while (P < p.nB) P <<= 1;
+  hipLaunchKernelGGL(route_kernel, dim3((unsigned)p.rows), dim3(kRouteThreads), 0, s, m.scores,
+                     p.nB, p.words, P, prm.top_p, prm.topk_floor, m.bitmask, m.row_count,
+                     m.col_idx, m.head_count, wflags);
+  if (prm.aug_budget > 0) {
+    hipLaunchKernelGGL(topup_select_kernel, dim3(nheads), dim3(kSelThreads), 0, s, m.scores,
+                       m.bitmask, m.head_count, p.nB, p.words, (int64_t)prm.aug_budget, thresh);
+    hipLaunchKernelGGL(topup_apply_kernel, dim3((unsigned)p.rows), dim3(kRouteThreads), 0, s,
+                       m.scores, p.nB, p.words, thresh, m.bitmask, m.row_count, m.col_idx,
+                       m.head_count);
+  }
+  hipLaunchKernelGGL(queue_kernel, dim3(1), dim3(kQThreads), 0, s, m.row_count, p.rows, p.nB,
+                     m.queue);
+  return hip_fail(hipGetLastError(), "route launch");
+}
+
+}  // namespace fva

@@ -1,0 +1,202 @@
+/*
+ * fva.h - C ABI of libfva, adaptive block-sparse self-attention for video
+ * diffusion transformers on AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow "FVAttn: Adaptive Sparse Attention with Runtime Load
+ * Balancing for Video Generation" (papers.paperslantern.ai/papers/2607.16190):
+ *   - video-aware block organization of the T x H x W latent token grid
+ *     (section 3.1),
+ *   - the sparse-routing frontend: block similarities from pooled Q/K, a Top-p
+ *     CDF threshold with a Top-k safety floor, per-head workload and the
+ *     key-block importance order (sections 2 and 3.1),
+ *   - slack-aware augmentation, here a per-head top-up of further high-score
+ *     blocks up to a pair budget (section 3.3),
+ *   - block-sparse attention in which only selected query-key block pairs are
+ *     evaluated (section 2), run as a persistent kernel over a heaviest-first
+ *     work queue, the one-GPU counterpart of runtime load balancing
+ *     (section 3.2).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates or frees device memory.
+ *   - Work is enqueued on `stream`; no call synchronizes with the host.
+ *   - Arguments are validated on the host before anything is launched.  A
+ *     negative fva_status is returned on failure and fva_last_error() gives a
+ *     thread-local message.  Nothing is launched when validation fails.
+ *   - bf16 tensors are IEEE bfloat16 stored as uint16.
+ *   - Supported: head dim d in {64, 128}; block size BLK = bt*bh*bw in
+ *     {64, 128}; number of blocks nB <= 2048; B*Hh*nB < 2^31.  Other shapes
+ *     return FVA_ERR_UNSUPPORTED.
+ *   - Calls are reentrant (no global mutable state) apart from the per-thread
+ *     error string.
+ *
+ * Shapes (N = T*H*W tokens, BLK tokens per block, nB = ceil(N/BLK) blocks,
+ * Npad = nB*BLK):
+ *   token-major   [B, N, Hh, d]  the DiT layout, element strides given by caller
+ *   rows          [B, Hh, Npad, d] reordered, contiguous, pad rows zero
+ *   vt64          [B, Hh, Npad/64, d, 64] reordered V, each chunk of 64
+ *                 consecutive reordered tokens stored d-major; inside a chunk
+ *                 the token slot is the token offset with bits 2 and 3
+ *                 swapped (a layout chosen for the MFMA operand order).
+ */
+#ifndef FVA_H
+#define FVA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FVA_OK = 0,
+  FVA_ERR_INVALID_ARG = -1,   /* null pointer, non-positive size, bad flag   */
+  FVA_ERR_UNSUPPORTED = -2,   /* valid but outside the supported shapes      */
+  FVA_ERR_WORKSPACE = -3,     /* workspace missing or too small              */
+  FVA_ERR_HIP = -4            /* a HIP runtime call or launch failed         */
+} fva_status;
+
+/* Latent grid T x H x W and block shape bt x bh x bw (section 3.1). */
+typedef struct {
+  int32_t T, H, W;
+  int32_t bt, bh, bw;
+} fva_grid;
+
+/* Derived sizes of a problem. */
+typedef struct {
+  int64_t N;                 /* tokens                                      */
+  int64_t Npad;              /* nB * BLK                                    */
+  int32_t BLK;               /* tokens per block                            */
+  int32_t nB;                /* blocks per head                             */
+  int32_t words;             /* 32-bit words per bitmask row = ceil(nB/32)   */
+  int32_t reserved;
+  int64_t rows;              /* B*Hh*nB routing rows = attention work items  */
+  size_t route_ws_bytes;     /* workspace fva_route needs                    */
+  size_t attn_ws_bytes;      /* workspace fva_sparse_attn needs              */
+  size_t trace_bytes;        /* bytes of an FVA_TRACE buffer (32 per item)   */
+} fva_sizes_t;
+
+/* Routing parameters (sections 2 and 3.1; top-up: section 3.3). */
+typedef struct {
+  float top_p;               /* Top-p threshold, used at its float32 value.
+                                p >= 1 keeps every block, p <= 0 none.       */
+  int32_t topk_floor;        /* Top-k safety floor, absolute block count >= 0 */
+  int64_t aug_budget;        /* per-head pair budget for the top-up; 0 = off  */
+  float scale;               /* score scale; <= 0 selects 1/sqrt(d)          */
+  int32_t reserved;
+} fva_route_params;
+
+/* The block mask and its derived metadata; all DEVICE pointers, caller-owned.
+ * Row index r = (b*Hh + h)*nB + i for query block i of head h in batch b.   */
+typedef struct {
+  float* scores;             /* [rows, nB] float32 pooled block scores       */
+  uint32_t* bitmask;         /* [rows, words]; bit j%32 of word j/32 = M(h,i,j) */
+  int32_t* row_count;        /* [rows] selected key blocks per row            */
+  int16_t* col_idx;          /* [rows, nB] selected key blocks, ascending;
+                                entries past row_count are unspecified       */
+  int32_t* head_count;       /* [B*Hh] W_h = selected pairs of the head       */
+  int32_t* queue;            /* [rows] row ids, row_count descending, ties by
+                                row id ascending (heaviest first)            */
+} fva_mask;
+
+/* fva_route flags */
+#define FVA_ROUTE_SCORES_IN 0x1  /* skip pooling and scoring: route from
+                                    mask->scores as given                    */
+
+/* fva_sparse_attn flags: schedule of (head, query-block) work items */
+#define FVA_SCHED_QUEUE  0x0  /* persistent workgroups pop the heaviest-first
+                                 queue through an atomic counter (default)   */
+#define FVA_SCHED_STATIC 0x1  /* persistent workgroups take contiguous runs of
+                                 rows in row order (fixed placement)         */
+#define FVA_SCHED_GRID   0x2  /* one workgroup per queue entry, hardware
+                                 dispatch                                    */
+#define FVA_TRACE        0x10 /* write one trace record per item             */
+
+/* fva_reorder directions and layouts */
+#define FVA_FORWARD 0
+#define FVA_INVERSE 1
+#define FVA_LAYOUT_ROWS 0
+#define FVA_LAYOUT_VT64 1
+
+/* Sizes of a problem and the workspaces it needs.  B, Hh > 0; d as above.
+ * Returns FVA_ERR_UNSUPPORTED for shapes outside the supported set.        */
+fva_status fva_sizes(const fva_grid* grid, int32_t B, int32_t Hh, int32_t d,
+                     fva_sizes_t* out);
+
+/* Video-aware block organization (section 3.1).  Reordered position r holds
+ * the token visited r-th when tiles of bt x bh x bw are walked in raster
+ * order (tile frame, tile row, tile column; edge tiles clipped) and tokens
+ * inside a tile in raster order (t, y, x).  Positions N..Npad-1 are padding.
+ *
+ * FVA_FORWARD: src is token-major [B, N, Hh, d] with element strides
+ *   strides[0..2] for (b, n, h) and unit channel stride; dst is `rows`
+ *   (layout FVA_LAYOUT_ROWS, pad rows written as zero) or `vt64`
+ *   (FVA_LAYOUT_VT64, pad tokens zero).
+ * FVA_INVERSE: src is `rows`; dst is token-major [B, N, Hh, d] with element
+ *   strides strides[0..2]; pad rows are dropped.  Layout must be ROWS.
+ * Pointers and strides must be 16-byte aligned (strides multiples of 8).
+ * src and dst must not overlap.                                             */
+fva_status fva_reorder(const void* src, void* dst, int32_t B, int32_t Hh, int32_t d,
+                       const fva_grid* grid, const int64_t strides[3],
+                       int32_t direction, int32_t layout, hipStream_t stream);
+
+/* Sparse-routing frontend (sections 2 and 3.1; top-up section 3.3).
+ * qr, kr: `rows` layout bf16.  For every row (b, h, i):
+ *   1. unless FVA_ROUTE_SCORES_IN: qbar, kbar = mean of each block's real
+ *      tokens; scores[r, j] = (qbar_i . kbar_j) * scale in float32;
+ *   2. importance order = key blocks by score descending, ties by index
+ *      ascending (-0 == +0);
+ *   3. float64 softmax of the row accumulated along that order; the Top-p set
+ *      is the shortest prefix whose cumulative share reaches top_p; the row
+ *      keeps max(that length, topk_floor) blocks, at most nB;
+ *   4. bitmask, row_count, col_idx and head_count are written;
+ *   5. if aug_budget > 0, every head whose W_h is below the budget gains the
+ *      (aug_budget - W_h) unselected pairs of highest score (ties: query block
+ *      ascending, then key block ascending) and its rows are rewritten;
+ *   6. queue = rows ordered heaviest first.
+ * ws must hold fva_sizes().route_ws_bytes bytes, 256-byte aligned.  A NaN
+ * score sets bit 0 of the first 32-bit word of ws (read it with
+ * fva_route_flags after the stream completes); routing of that row is then
+ * unspecified but stays in bounds.                                          */
+fva_status fva_route(const void* qr, const void* kr, int32_t B, int32_t Hh, int32_t d,
+                     const fva_grid* grid, const fva_route_params* params,
+                     const fva_mask* mask, void* ws, size_t ws_bytes, int32_t flags,
+                     hipStream_t stream);
+
+/* Copies the routing status word from a route workspace to *flags_out (host)
+ * synchronously on `stream`.  Bit 0: a NaN score was seen.                 */
+fva_status fva_route_flags(const void* ws, uint32_t* flags_out, hipStream_t stream);
+
+/* Block-sparse attention (section 2: only selected query-key block pairs are
+ * evaluated).  For each real query token of block i of head (b, h):
+ *   out = sum over the real keys of the selected key blocks of
+ *         softmax_k((q . k) * scale) * v_k,
+ * computed with bf16 MFMA products, float32 accumulation and an online
+ * softmax.  Rows with no selected block, and pad rows, are written as zero.
+ * qr, kr: `rows` bf16; vt: `vt64` bf16; out: `rows` bf16.
+ * scale <= 0 selects 1/sqrt(d).  flags: one FVA_SCHED_* value, optionally
+ * | FVA_TRACE.  ws: fva_sizes().attn_ws_bytes bytes (scheduler counter).
+ * trace (with FVA_TRACE): trace_bytes bytes; record k (8 x uint32) describes
+ * the k-th processed queue entry: {row, XCC_ID, HW_ID, workgroup id,
+ * t0 lo, t0 hi, t1 lo, t1 hi} with t = s_memrealtime ticks (100 MHz).     */
+fva_status fva_sparse_attn(const void* qr, const void* kr, const void* vt, void* out,
+                           int32_t B, int32_t Hh, int32_t d, const fva_grid* grid,
+                           const fva_mask* mask, float scale, int32_t flags,
+                           void* ws, size_t ws_bytes, void* trace, hipStream_t stream);
+
+/* Dense attention over every key block with the same core: the comparator
+ * for the sparse kernel.  Same layouts and output convention as above.     */
+fva_status fva_dense_attn(const void* qr, const void* kr, const void* vt, void* out,
+                          int32_t B, int32_t Hh, int32_t d, const fva_grid* grid,
+                          float scale, hipStream_t stream);
+
+/* Human-readable status name, and the calling thread's last error detail. */
+const char* fva_status_string(fva_status s);
+const char* fva_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FVA_H */

@@ -1,0 +1,93 @@
+"""The C-ABI library loads and exports every entry point include/fva.h
+declares; host-side sizing and validation (no GPU needed: nothing here
+launches a kernel)."""
+
+import ctypes
+import os
+
+import pytest
+
+from adaptive_block_sparse_reorder_amd import fva as F
+from adaptive_block_sparse_reorder_amd.inputs import WORKLOADS
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(F.LIB_PATH):
+        from adaptive_block_sparse_reorder_amd import build
+        build.build(verbose=False)
+    return F.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = F.header_functions()
+    assert set(names) >= {"fva_sizes", "fva_reorder", "fva_route", "fva_sparse_attn",
+                          "fva_dense_attn", "fva_status_string", "fva_last_error"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+@pytest.mark.parametrize("name,N,Npad,nB,words", [
+    ("tiny", 1280, 1280, 20, 1), ("480p", 32760, 32768, 256, 8),
+    ("720p", 75600, 75648, 591, 19), ("hetero", 75600, 75648, 591, 19),
+    ("long720p", 111600, 111616, 872, 28)])
+def test_sizes_match_workloads(lib, name, N, Npad, nB, words):
+    w = WORKLOADS[name]
+    s = F.fva_sizes(F.make_grid(w.grid, w.block), w.B, w.Hh, w.d)
+    assert (s.N, s.Npad, s.nB, s.words, s.BLK) == (N, Npad, nB, words, w.BLK)
+    assert s.rows == w.B * w.Hh * nB
+    assert s.trace_bytes == 32 * s.rows
+    # route workspace: status word + pooled q, k (float32) + per-head thresholds
+    assert s.route_ws_bytes >= 256 + 2 * 4 * s.rows * w.d + 8 * w.Hh
+
+
+def test_derived_floor_and_budget():
+    assert WORKLOADS["720p"].topk_floor == 48          # ceil(0.08 * 591)
+    assert WORKLOADS["long720p"].aug_budget == 190096  # 25 % of 872^2 pairs
+
+
+def test_validation_errors_before_launch(lib):
+    g = F.make_grid((5, 16, 16), (1, 8, 8))
+    out = F.fva_sizes_t()
+    assert lib.fva_sizes(ctypes.byref(g), 1, 2, 96, ctypes.byref(out)) == F.FVA_ERR_UNSUPPORTED
+    assert b"head dim" in lib.fva_last_error()
+    bad = F.make_grid((5, 16, 16), (1, 4, 8))       # 32-token blocks
+    assert lib.fva_sizes(ctypes.byref(bad), 1, 2, 64, ctypes.byref(out)) == F.FVA_ERR_UNSUPPORTED
+    neg = F.make_grid((0, 16, 16), (1, 8, 8))
+    assert lib.fva_sizes(ctypes.byref(neg), 1, 2, 64, ctypes.byref(out)) == F.FVA_ERR_INVALID_ARG
+    big = F.make_grid((64, 64, 64), (1, 8, 8))      # 4096 blocks
+    assert lib.fva_sizes(ctypes.byref(big), 1, 2, 64, ctypes.byref(out)) == F.FVA_ERR_UNSUPPORTED
+    st = (ctypes.c_int64 * 3)(1280 * 2 * 64, 2 * 64, 64)
+    # null pointers
+    assert lib.fva_reorder(None, None, 1, 2, 64, ctypes.byref(g), st, 0, 0, None) == \
+        F.FVA_ERR_INVALID_ARG
+    # misaligned stride
+    st2 = (ctypes.c_int64 * 3)(1280 * 2 * 64, 2 * 64, 63)
+    assert lib.fva_reorder(16, 32, 1, 2, 64, ctypes.byref(g), st2, 0, 0, None) == \
+        F.FVA_ERR_INVALID_ARG
+    # inverse into the vt64 layout is not a thing
+    assert lib.fva_reorder(16, 32, 1, 2, 64, ctypes.byref(g), st, 1, 1, None) == \
+        F.FVA_ERR_INVALID_ARG
+    # route: workspace too small, negative floor, bad flags
+    m = F.fva_mask(16, 16, 16, 16, 16, 16)
+    prm = F.fva_route_params(0.9, 2, 0, 0.0, 0)
+    assert lib.fva_route(16, 16, 1, 2, 64, ctypes.byref(g), ctypes.byref(prm), ctypes.byref(m),
+                         256, 8, 0, None) == F.FVA_ERR_WORKSPACE
+    prm2 = F.fva_route_params(0.9, -1, 0, 0.0, 0)
+    assert lib.fva_route(16, 16, 1, 2, 64, ctypes.byref(g), ctypes.byref(prm2), ctypes.byref(m),
+                         256, 1 << 30, 0, None) == F.FVA_ERR_INVALID_ARG
+    assert lib.fva_route(16, 16, 1, 2, 64, ctypes.byref(g), ctypes.byref(prm), ctypes.byref(m),
+                         256, 1 << 30, 0x8, None) == F.FVA_ERR_INVALID_ARG
+    m0 = F.fva_mask(16, 0, 16, 16, 16, 16)
+    assert lib.fva_route(16, 16, 1, 2, 64, ctypes.byref(g), ctypes.byref(prm), ctypes.byref(m0),
+                         256, 1 << 30, 0, None) == F.FVA_ERR_INVALID_ARG
+    # attention: bad schedule flag, missing workspace, trace without buffer
+    assert lib.fva_sparse_attn(16, 16, 16, 16, 1, 2, 64, ctypes.byref(g), ctypes.byref(m), 0.0,
+                               0x3, 256, 256, None, None) == F.FVA_ERR_INVALID_ARG
+    assert lib.fva_sparse_attn(16, 16, 16, 16, 1, 2, 64, ctypes.byref(g), ctypes.byref(m), 0.0,
+                               0, None, 0, None, None) == F.FVA_ERR_WORKSPACE
+    assert lib.fva_sparse_attn(16, 16, 16, 16, 1, 2, 64, ctypes.byref(g), ctypes.byref(m), 0.0,
+                               F.FVA_TRACE, 256, 256, None, None) == F.FVA_ERR_INVALID_ARG
+    assert lib.fva_dense_attn(16, 16, 0, 16, 1, 2, 64, ctypes.byref(g), 0.0, None) == \
+        F.FVA_ERR_INVALID_ARG
+    assert lib.fva_status_string(F.FVA_ERR_WORKSPACE) == b"FVA_ERR_WORKSPACE"
