@@ -1,14 +1,14 @@
 // Block-sparse flash attention for gfx950 (FVAttn page, section 2: only the
 // selected query-key block pairs are evaluated; section 3.2: work is balanced
-// on the realized per-row workload, here by a persistent heaviest-first queue).
+// on the realized per-row workload, here by persistent work queues).
 //
-// Work item = one query block (BLK rows) of one head.  A workgroup has two
-// groups of BLK/32 waves; each wave owns 32 queries.  The selected key blocks
-// of the row are cut into 64-key sub-tiles; a pipeline stage holds two
-// sub-tiles (one per group) of K and V in LDS, double-buffered and filled by
-// direct HBM->LDS loads (global_load_lds_dwordx4), so each group runs its own
-// online softmax over half of the sub-tiles and the two partial results are
-// merged through LDS at the end of the item.
+// Work item = one query block (BLK rows) of one head, processed by one
+// workgroup of BLK/32 waves; each wave owns 32 queries and walks every
+// selected key block of the row in 64-key sub-tiles.  A sub-tile of K and V
+// (32 KB at d=128) is staged in LDS by direct HBM->LDS loads
+// (global_load_lds_dwordx4), double-buffered, so a workgroup uses 64 KB and
+// two independent workgroups share a CU: while one is in its softmax the
+// other keeps the matrix cores busy.
 //
 // Products use v_mfma_f32_32x32x16_bf16 in transposed form:
 //   S^T (keys x queries) = K * Q^T     A = K from LDS, B = Q^T in registers
@@ -18,6 +18,19 @@
 // exchange per tile for the max).  P^T leaves the S accumulator in exactly the
 // B-operand order the PV product needs once the V^T chunk stores key slots
 // with bits 2 and 3 swapped (done by the reorder kernel).
+//
+// Online softmax in the log2 domain with the scale folded into one FMA per
+// score, and a lazy rescale: the running reference max only moves (and O and
+// the running sum are rescaled) when a tile's max exceeds it by more than
+// 2^8, so exponentials stay <= 256 and most tiles skip the rescale.
+//
+// Schedules: static contiguous split (fixed placement), hardware grid over the
+// heaviest-first queue, a persistent atomic heaviest-first queue, and an
+// XCD-aware persistent schedule: heads are assigned to the 8 XCDs by
+// longest-processing-time on their realized workload W_h, each XCD walks its
+// heads' rows heaviest first (rows of one head stay together so their K/V
+// stream through that XCD's L2), and a workgroup whose XCD runs dry steals
+// from the other XCDs' queues.
 #include <algorithm>
 
 #include "fva_internal.hpp"
@@ -26,20 +39,22 @@ namespace fva {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int KT = 64;  // keys per sub-tile
+constexpr int KT = 64;           // keys per sub-tile
+constexpr int NXCD = 8;          // XCDs; workgroup b is dispatched to XCD b % 8
+constexpr float kLazy = 8.0f;    // log2-domain slack before the reference max moves
 
-__device__ __forceinline__ uint32_t f2bf_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
-  return __builtin_bit_cast(bf16x8, v);
-}
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ void g2lds16(const void* g, char* lds_uniform) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_uniform, 16, 0,
@@ -54,15 +69,31 @@ __device__ __forceinline__ int swz_k(int r) {
 }
 __device__ __forceinline__ int swz_v(int r) { return (r >> 1) & 7; }
 
+// Attention workspace: [0,256) counters and per-XCD offsets, then per-head
+// bases, then the XCD-ordered row list.
+struct AttnWs {
+  static constexpr int kQueueCtr = 0;      // int: global queue counter
+  static constexpr int kXcdCtr = 16;       // int[8]: per-XCD counters
+  static constexpr int kXcdOff = 32;       // int[9]: per-XCD offsets into xq
+  __host__ __device__ static size_t head_base_off() { return 256; }
+  __host__ __device__ static size_t xq_off(int64_t nheads) {
+    return 256 + ((nheads * 4 + 255) & ~(int64_t)255);
+  }
+  __host__ __device__ static size_t bytes(int64_t nheads, int64_t rows) {
+    return xq_off(nheads) + ((rows * 4 + 255) & ~(int64_t)255);
+  }
+};
+
 struct AttnArgs {
   const uint16_t* qr;
   const uint16_t* kr;
   const uint16_t* vt;
   uint16_t* out;
   const int32_t* row_count;
+  const int32_t* head_count;
   const int16_t* col_idx;
-  const int32_t* queue;
-  int32_t* counter;
+  const int32_t* queue;    // heaviest-first queue, or the XCD-ordered list
+  int32_t* ws;             // attention workspace (int view)
   uint32_t* trace;
   int64_t N, Npad;
   int64_t rows;
@@ -70,39 +101,89 @@ struct AttnArgs {
   float sl2;  // scale * log2(e)
 };
 
-template <int D, int BLK, int SCHED, bool DENSE, bool TRACE>
-__global__ __launch_bounds__(BLK * 4) void attn_kernel(AttnArgs a) {
-  constexpr int NT = BLK * 4;            // threads
-  constexpr int NW = NT / 64;            // waves
-  constexpr int GW = NW / 2;             // waves per group
+// QT = 32-query tiles per wave (1: 4 waves of 32 queries per 128-row block,
+// two waves per SIMD; 2: 2 waves of 64 queries, one wave per SIMD).
+template <int QT>
+constexpr int attn_threads(int blk) { return blk / (32 * QT) * 64; }
+
+template <int D, int BLK, int QT, int SCHED, bool DENSE, bool TRACE>
+__global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_per_eu(
+    QT == 1 ? 2 : 1, QT == 1 ? 2 : 1))) void attn_kernel(AttnArgs a) {
+  constexpr int NT = attn_threads<QT>(BLK);  // threads: BLK/(32*QT) waves
+  constexpr int NW = NT / 64;
   constexpr int TILE = KT * D * 2;       // bytes of one K or V^T sub-tile
-  constexpr int STAGE = 4 * TILE;        // K0, V0, K1, V1
   constexpr int NSUB = BLK / KT;         // sub-tiles per key block
   constexpr int KSTEPS = D / 16;         // MFMA k-steps over the head dim
   constexpr int DT = D / 32;             // 32-row tiles of the head dim
   constexpr int CPR = D / 8;             // 16-byte chunks per K row
-  constexpr int LOADS = STAGE / 16 / NT; // 16-byte loads per thread per stage
-  static_assert(LOADS * 16 * NT == STAGE, "stage size");
-  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
+  constexpr int LOADS = TILE / 16 / NT;  // 16-byte loads per thread per K (or V) tile
+  static_assert(LOADS * 16 * NT == TILE, "tile size");
+  // LDS: K tiles at [0, 2*TILE), V^T tiles at [2*TILE, 4*TILE)
+  __shared__ __attribute__((aligned(16))) char lds[4 * TILE];
+  __shared__ int16_t s_cols[2048];
   __shared__ int s_item;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave / GW;             // 0 or 1
-  const int wq = wave % GW;              // query sub-block of this wave
   const int l32 = lane & 31;
   const int hl = lane >> 5;
+
+  // per-thread element offsets of its 16-byte loads inside a K and a V^T tile
+  int koff[LOADS], voff[LOADS];
+#pragma unroll
+  for (int k = 0; k < LOADS; ++k) {
+    const int slot = (k * NW + wave) * 64 + lane;
+    {
+      const int r = slot / CPR, p = slot % CPR;
+      koff[k] = r * D + ((p ^ swz_k<D>(r)) * 8);
+    }
+    {
+      const int r = slot / 8, p = slot % 8;
+      voff[k] = r * KT + ((p ^ swz_v(r)) * 8);
+    }
+  }
+
+  const int xcd = blockIdx.x % NXCD;
+  int victim = 0;  // XCD schedule: how far thread 0 has moved from its own XCD
+
+  // fetch the next item (position in the schedule's row list); -1 when done
+  auto fetch = [&]() -> int64_t {
+    if (SCHED == FVA_SCHED_QUEUE) {
+      if (tid == 0) s_item = atomicAdd(a.ws + AttnWs::kQueueCtr, 1);
+      __syncthreads();
+      const int64_t it = s_item;
+      return it < a.rows ? it : -1;
+    } else {  // FVA_SCHED_XCD
+      if (tid == 0) {
+        int got = -1;
+        while (victim < NXCD) {
+          const int y = (xcd + victim) % NXCD;
+          const int beg = a.ws[AttnWs::kXcdOff + y], end = a.ws[AttnWs::kXcdOff + y + 1];
+          if (end > beg) {
+            const int it = atomicAdd(a.ws + AttnWs::kXcdCtr + y, 1);
+            if (it < end - beg) { got = beg + it; break; }
+          }
+          ++victim;
+        }
+        s_item = got;
+      }
+      __syncthreads();
+      return s_item;
+    }
+  };
 
   int64_t item, item_end = 0;
   if (SCHED == FVA_SCHED_STATIC) {
     const int64_t G = gridDim.x;
     item = (int64_t)blockIdx.x * a.rows / G;
     item_end = ((int64_t)blockIdx.x + 1) * a.rows / G;
-  } else if (SCHED == FVA_SCHED_QUEUE) {
-    if (tid == 0) s_item = atomicAdd(a.counter, 1);
-    __syncthreads();
-    item = s_item;
+  } else if (SCHED == FVA_SCHED_QUEUE || SCHED == FVA_SCHED_XCD) {
+    item = fetch();
+  } else if (DENSE) {
+    // XCD-aware remap: XCD x walks a contiguous range of rows (whole heads)
+    const int64_t b = blockIdx.x;
+    item = (a.rows % NXCD == 0) ? (b % NXCD) * (a.rows / NXCD) + b / NXCD : b;
   } else {
     item = blockIdx.x;
   }
@@ -110,7 +191,7 @@ __global__ __launch_bounds__(BLK * 4) void attn_kernel(AttnArgs a) {
   while (true) {
     if (SCHED == FVA_SCHED_STATIC) {
       if (item >= item_end) break;
-    } else if (item >= a.rows) {
+    } else if (item < 0 || item >= a.rows) {
       break;
     }
     uint64_t t_start = 0;
@@ -122,109 +203,131 @@ __global__ __launch_bounds__(BLK * 4) void attn_kernel(AttnArgs a) {
     const int64_t bh = row / a.nB;
     const int qb = (int)(row - bh * a.nB);
     const int cnt = DENSE ? a.nB : __builtin_amdgcn_readfirstlane(a.row_count[row]);
-    const int16_t* cols = a.col_idx + row * a.nB;
+    if (!DENSE) {
+      const int16_t* cols = a.col_idx + row * a.nB;
+      for (int t = tid; t < cnt; t += NT) s_cols[t] = cols[t];
+      __syncthreads();
+    }
     const int64_t nlast = a.N - (int64_t)(a.nB - 1) * BLK;  // real keys of the last block
     int U = cnt * NSUB;
     if (cnt > 0) {
-      const int lastcol = DENSE ? a.nB - 1 : (int)cols[cnt - 1];
+      const int lastcol = DENSE ? a.nB - 1 : (int)s_cols[cnt - 1];
       if (lastcol == a.nB - 1) U -= NSUB - (int)((nlast + KT - 1) / KT);
     }
-    const int nstage = (U + 1) >> 1;
+    U = __builtin_amdgcn_readfirstlane(U);
 
     const uint16_t* kbase = a.kr + bh * a.Npad * D;
-    const uint16_t* vbase = a.vt + bh * a.Npad * D;  // vt64: chunk c at c*64*D
+    const uint16_t* vbase = a.vt + bh * a.Npad * D;  // vt64 chunk of key0 at key0*D
 
-    // issue the loads of stage s into buffer s&1
-    auto load_stage = [&](int s) {
-      char* buf = lds + (s & 1) * STAGE;
+    auto key0_of = [&](int u) -> int64_t {
+      const int t = u / NSUB, half = u % NSUB;
+      const int kb = DENSE ? t : __builtin_amdgcn_readfirstlane((int)s_cols[t]);
+      return (int64_t)kb * BLK + half * KT;
+    };
+    auto load_k = [&](int u) {
+      char* buf = lds + (u & 1) * TILE;
+      const uint16_t* src = kbase + key0_of(u) * D;
 #pragma unroll
-      for (int k = 0; k < LOADS; ++k) {
-        const int L0 = (k * NW + wave) * 64;        // first chunk of this wave's group
-        const int part = L0 / (TILE / 16);          // 0:K0 1:V0 2:K1 3:V1
-        const int g = part >> 1;
-        const int u = 2 * s + g;
-        if (u >= U) continue;                       // wave-uniform
-        const int t = u / NSUB, half = u % NSUB;
-        const int kb = DENSE ? t : (int)cols[t];
-        const int64_t key0 = (int64_t)kb * BLK + half * KT;
-        const int slot = (L0 % (TILE / 16)) + lane;
-        const void* src;
-        if ((part & 1) == 0) {
-          const int r = slot / CPR, p = slot % CPR;
-          const int c = p ^ swz_k<D>(r);
-          src = kbase + (key0 + r) * D + c * 8;
-        } else {
-          const int r = slot / 8, p = slot % 8;
-          const int c = p ^ swz_v(r);
-          src = vbase + (key0 / KT) * (int64_t)(KT * D) + r * KT + c * 8;
-        }
-        g2lds16(src, buf + L0 * 16);
-      }
+      for (int k = 0; k < LOADS; ++k) g2lds16(src + koff[k], buf + (k * NW + wave) * 1024);
+    };
+    auto load_v = [&](int u) {
+      char* buf = lds + (2 + (u & 1)) * TILE;
+      const uint16_t* src = vbase + key0_of(u) * D;
+#pragma unroll
+      for (int k = 0; k < LOADS; ++k) g2lds16(src + voff[k], buf + (k * NW + wave) * 1024);
     };
 
-    // Q^T operand: this wave's 32 queries, lane holds query l32, d chunk 2kk+hl
-    const int64_t q0 = (int64_t)qb * BLK + wq * 32;
-    bf16x8 qop[KSTEPS];
-    {
-      const uint16_t* qp = a.qr + (bh * a.Npad + q0 + l32) * D + hl * 8;
+    // Q^T operands: q-tile j of this wave = 32 queries; lane holds query l32, d chunk 2kk+hl
+    const int64_t q0 = (int64_t)qb * BLK + wave * 32 * QT;
+    bf16x8 qop[QT][KSTEPS];
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) qop[kk] = as_bf16x8(*(const u32x4*)(qp + kk * 16));
+    for (int j = 0; j < QT; ++j) {
+      const uint16_t* qp = a.qr + (bh * a.Npad + q0 + 32 * j + l32) * D + hl * 8;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) qop[j][kk] = as_bf16x8(*(const u32x4*)(qp + kk * 16));
     }
 
-    f32x16 oacc[DT];
+    f32x16 oacc[DT][QT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+      for (int j = 0; j < QT; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][j][r] = 0.f;
+    float m_use[QT], l_run[QT];
+#pragma unroll
+    for (int j = 0; j < QT; ++j) { m_use[j] = -INFINITY; l_run[j] = 0.f; }
 
-    if (nstage > 0) load_stage(0);
-    for (int s = 0; s < nstage; ++s) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (s + 1 < nstage) load_stage(s + 1);
-      const int u = 2 * s + grp;
-      if (u < U) {
-        const char* kt = lds + (s & 1) * STAGE + (2 * grp) * TILE;
-        const char* vtile = kt + TILE;
-        // S^T = K Q^T for keys 32m + (row) of this sub-tile
-        f32x16 sacc[2];
+    // S^T of sub-tile u: keys 32m + (acc row) x queries 32j + l32
+    auto qk = [&](int u, f32x16 (&s)[2][QT]) {
+      const char* kt = lds + (u & 1) * TILE;
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
+      for (int m = 0; m < 2; ++m) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[m][r] = 0.f;
-          const int kr_ = 32 * m + l32;
+        for (int j = 0; j < QT; ++j)
 #pragma unroll
-          for (int kk = 0; kk < KSTEPS; ++kk) {
-            const int c = (2 * kk + hl) ^ swz_k<D>(kr_);
-            const bf16x8 kop = as_bf16x8(*(const u32x4*)(kt + kr_ * (D * 2) + c * 16));
-            sacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[kk], sacc[m], 0, 0, 0);
-          }
+          for (int r = 0; r < 16; ++r) s[m][j][r] = 0.f;
+        const int kr_ = 32 * m + l32;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+          const int c = (2 * kk + hl) ^ swz_k<D>(kr_);
+          const bf16x8 kop = as_bf16x8(*(const u32x4*)(kt + kr_ * (D * 2) + c * 16));
+#pragma unroll
+          for (int j = 0; j < QT; ++j)
+            s[m][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[j][kk], s[m][j], 0, 0, 0);
         }
-        // keys of this sub-tile that are real
-        const int t = u / NSUB, half = u % NSUB;
-        const int kb = DENSE ? t : (int)cols[t];
-        const int64_t key0 = (int64_t)kb * BLK + half * KT;
-        const int kvalid = (int)min((int64_t)KT, a.N - key0);
-        float mx = -INFINITY;
+      }
+    };
+    // masking of padded keys, tile max and lazy rescale for sub-tile u
+    auto prep = [&](int u, f32x16 (&s)[2][QT]) {
+      const int kvalid = (int)min((int64_t)KT, a.N - key0_of(u));
+      if (kvalid < KT) {
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float x = sacc[m][r] * a.sl2;
-            if (kvalid < KT) {
+          for (int j = 0; j < QT; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
               const int key = 32 * m + 8 * (r >> 2) + 4 * hl + (r & 3);
-              if (key >= kvalid) x = -INFINITY;
+              if (key >= kvalid) s[m][j][r] = -INFINITY;
             }
-            sacc[m][r] = x;
-            mx = fmaxf(mx, x);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        float psum = 0.f;
-        bf16x8 pop[2][2];
+      }
+      float mx[QT];
+      bool grow = false;
+#pragma unroll
+      for (int j = 0; j < QT; ++j) {
+        float v = fmaxf(s[0][j][0], s[0][j][1]);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int r = (m == 0 ? 2 : 0); r < 16; ++r) v = fmaxf(v, s[m][j][r]);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                         false, false);
+        mx[j] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.sl2;
+        grow = grow || (mx[j] > m_use[j] + kLazy);
+      }
+      // move the reference max only when a tile exceeds it by 2^8
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+        for (int j = 0; j < QT; ++j) {
+          const float m_new = fmaxf(m_use[j], mx[j]);
+          const float alpha = __builtin_amdgcn_exp2f(m_use[j] - m_new);
+          l_run[j] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[dt][j][r] *= alpha;
+          m_use[j] = m_new;
+        }
+      }
+    };
+    // probabilities of sub-tile u as PV B-operands, and their bf16 sum
+    auto probs = [&](const f32x16 (&s)[2][QT], bf16x8 (&pop)[2][2][QT]) {
+      const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int j = 0; j < QT; ++j) {
+        const float nm = -m_use[j];
+        float ls = l_run[j];
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -232,72 +335,85 @@ __global__ __launch_bounds__(BLK * 4) void attn_kernel(AttnArgs a) {
             u32x4 pk;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float p0 = __builtin_amdgcn_exp2f(sacc[m][8 * b + 2 * e] - m_use);
-              const float p1 = __builtin_amdgcn_exp2f(sacc[m][8 * b + 2 * e + 1] - m_use);
-              psum += p0 + p1;
-              pk[e] = f2bf_rne(p0) | (f2bf_rne(p1) << 16);
+              const float p0 = __builtin_amdgcn_exp2f(fmaf(s[m][j][8 * b + 2 * e], a.sl2, nm));
+              const float p1 = __builtin_amdgcn_exp2f(fmaf(s[m][j][8 * b + 2 * e + 1], a.sl2, nm));
+              const uint32_t w = pack_bf16(p0, p1);
+              ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one2, ls, false);
+              pk[e] = w;
             }
-            pop[m][b] = as_bf16x8(pk);
+            pop[m][b][j] = as_bf16x8(pk);
           }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
+        l_run[j] = ls;
+      }
+    };
+    auto pv = [&](int u, const bf16x8 (&pop)[2][2][QT]) {
+      const char* vtile = lds + (2 + (u & 1)) * TILE;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt) {
+        const int vr = 32 * dt + l32;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-        // O^T += V^T P^T
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int vr = 32 * dt + l32;
+          for (int b = 0; b < 2; ++b) {
+            const int c = (4 * m + 2 * b + hl) ^ swz_v(vr);
+            const bf16x8 vop = as_bf16x8(*(const u32x4*)(vtile + vr * (KT * 2) + c * 16));
 #pragma unroll
-          for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-              const int c = (4 * m + 2 * b + hl) ^ swz_v(vr);
-              const bf16x8 vop = as_bf16x8(*(const u32x4*)(vtile + vr * (KT * 2) + c * 16));
-              oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[m][b], oacc[dt], 0, 0, 0);
-            }
-        }
+            for (int j = 0; j < QT; ++j)
+              oacc[dt][j] =
+                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[m][b][j], oacc[dt][j], 0, 0, 0);
+          }
+      }
+    };
+
+    if (U > 0) {
+      // prologue: K(0), V(0), K(1) in flight; S(0) once K(0) has landed
+      load_k(0);
+      load_v(0);
+      if (U > 1) load_k(1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      f32x16 sa[2][QT], sb[2][QT];
+      qk(0, sa);
+      // steady state: at iteration u, S(u) is in registers, K(u+1) and V(u)
+      // are (being) loaded; K(u+2) and V(u+1) are issued here.  S(u+1) is
+      // computed unconditionally (on a stale buffer after the last tile; the
+      // result is then unused) so the products of the next tile and the
+      // softmax of this one share one basic block.
+      auto step = [&](int u, f32x16 (&sc)[2][QT], f32x16 (&sn)[2][QT]) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (u + 2 < U) load_k(u + 2);
+        if (u + 1 < U) load_v(u + 1);
+        prep(u, sc);
+        bf16x8 pop[2][2][QT];
+        qk(u + 1, sn);
+        probs(sc, pop);
+        pv(u, pop);
+      };
+      for (int u = 0; u < U; u += 2) {
+        step(u, sa, sb);
+        if (u + 1 >= U) break;
+        step(u + 1, sb, sa);
       }
     }
-    // merge the two groups' partial results through LDS
-    __syncthreads();
-    float* mrg = (float*)lds + wq * (2 + 16 * DT) * 64;
-    if (grp == 1) {
-      mrg[0 * 64 + lane] = m_run;
-      mrg[1 * 64 + lane] = l_run;
+
+    // finalize: total sum over both half-waves, normalize, write bf16
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mrg[(2 + dt * 16 + r) * 64 + lane] = oacc[dt][r];
-    }
-    __syncthreads();
-    if (grp == 0) {
-      const float m1 = mrg[lane], l1 = mrg[64 + lane];
-      const float mm = fmaxf(m_run, m1);
-      const float mu = mm == -INFINITY ? 0.f : mm;
-      const float a0 = __builtin_amdgcn_exp2f(m_run - mu);
-      const float a1 = __builtin_amdgcn_exp2f(m1 - mu);
-      float l = l_run * a0 + l1 * a1;
-      l += __shfl_xor(l, 32, 64);
+    for (int j = 0; j < QT; ++j) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run[j]),
+                                                       __float_as_uint(l_run[j]), false, false);
+      const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       const float inv = l > 0.f ? 1.f / l : 0.f;
-      const int64_t q = q0 + l32;
-      const bool real = q < a.N;
+      const int64_t q = q0 + 32 * j + l32;
+      const float sc_ = q < a.N ? inv : 0.f;
       uint16_t* op = a.out + (bh * a.Npad + q) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           u32x2 w;
-          float v[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = 4 * i + j;
-            const float o = oacc[dt][r] * a0 + mrg[(2 + dt * 16 + r) * 64 + lane] * a1;
-            v[j] = real ? o * inv : 0.f;
-          }
-          w.x = f2bf_rne(v[0]) | (f2bf_rne(v[1]) << 16);
-          w.y = f2bf_rne(v[2]) | (f2bf_rne(v[3]) << 16);
+          w.x = pack_bf16(oacc[dt][j][4 * i + 0] * sc_, oacc[dt][j][4 * i + 1] * sc_);
+          w.y = pack_bf16(oacc[dt][j][4 * i + 2] * sc_, oacc[dt][j][4 * i + 3] * sc_);
           *(u32x2*)(op + 32 * dt + 8 * i + 4 * hl) = w;
         }
     }
@@ -313,29 +429,107 @@ __global__ __launch_bounds__(BLK * 4) void attn_kernel(AttnArgs a) {
       tr[6] = (uint32_t)t_end;
       tr[7] = (uint32_t)(t_end >> 32);
     }
-    // next item
+    // all waves are done with the LDS buffers and the column list
+    __syncthreads();
     if (SCHED == FVA_SCHED_STATIC) {
       ++item;
-      __syncthreads();
-    } else if (SCHED == FVA_SCHED_QUEUE) {
-      if (tid == 0) s_item = atomicAdd(a.counter, 1);
-      __syncthreads();
-      item = s_item;
+    } else if (SCHED == FVA_SCHED_QUEUE || SCHED == FVA_SCHED_XCD) {
+      item = fetch();
     } else {
       break;
     }
   }
 }
 
-__global__ void zero_counter(int32_t* c) { c[0] = 0; }
+__global__ void zero_counter(int32_t* ws) { ws[AttnWs::kQueueCtr] = 0; }
+
+// XCD plan, step 1 (one workgroup): order heads by W_h descending (ties by
+// head id), assign them greedily to the least-loaded XCD, and lay the XCD
+// row lists out contiguously: XCD x owns [off[x], off[x+1]) and its heads
+// follow in assignment order, nB rows each.
+constexpr int kPlanThreads = 256;
+constexpr int kMaxHeads = 4096;
+
+__global__ __launch_bounds__(kPlanThreads) void xcd_assign_kernel(const int32_t* head_count,
+                                                                  int nheads, int nB, int32_t* ws) {
+  __shared__ uint64_t keys[kMaxHeads];
+  __shared__ int16_t hx[kMaxHeads];
+  __shared__ int32_t hpos[kMaxHeads];
+  int P = 1;
+  while (P < nheads) P <<= 1;
+  for (int h = threadIdx.x; h < P; h += kPlanThreads)
+    keys[h] = h < nheads ? ((uint64_t)(~(uint32_t)head_count[h]) << 32) | (uint32_t)h : ~0ull;
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int q = threadIdx.x; q < P / 2; q += kPlanThreads) {
+        const int i = 2 * j * (q / j) + (q % j), l = i + j;
+        const uint64_t x = keys[i], y = keys[l];
+        if ((x > y) == ((i & k) == 0)) { keys[i] = y; keys[l] = x; }
+      }
+      __syncthreads();
+    }
+  if (threadIdx.x == 0) {
+    int64_t load[NXCD] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int nh[NXCD] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int r = 0; r < nheads; ++r) {
+      const int h = (int)(uint32_t)keys[r];
+      int best = 0;
+      for (int x = 1; x < NXCD; ++x)
+        if (load[x] < load[best]) best = x;
+      load[best] += head_count[h];
+      hx[h] = (int16_t)best;
+      hpos[h] = nh[best]++;
+    }
+    int off = 0;
+    for (int x = 0; x < NXCD; ++x) {
+      ws[AttnWs::kXcdOff + x] = off;
+      ws[AttnWs::kXcdCtr + x] = 0;
+      off += nh[x] * nB;
+    }
+    ws[AttnWs::kXcdOff + NXCD] = off;
+  }
+  __syncthreads();
+  int32_t* base = ws + AttnWs::head_base_off() / 4;
+  for (int h = threadIdx.x; h < nheads; h += kPlanThreads)
+    base[h] = ws[AttnWs::kXcdOff + hx[h]] + hpos[h] * nB;
+}
+
+// XCD plan, step 2 (one workgroup per head): the head's rows heaviest first
+// (row count descending, ties by query block ascending) at its base.
+__global__ __launch_bounds__(kPlanThreads) void xcd_fill_kernel(const int32_t* row_count, int nB,
+                                                                int32_t* ws, int64_t nheads) {
+  __shared__ uint32_t keys[2048];
+  const int64_t h = blockIdx.x;
+  int P = 1;
+  while (P < nB) P <<= 1;
+  for (int i = threadIdx.x; i < P; i += kPlanThreads)
+    keys[i] = i < nB ? ((uint32_t)(nB - row_count[h * nB + i]) << 11) | (uint32_t)i : ~0u;
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int q = threadIdx.x; q < P / 2; q += kPlanThreads) {
+        const int i = 2 * j * (q / j) + (q % j), l = i + j;
+        const uint32_t x = keys[i], y = keys[l];
+        if ((x > y) == ((i & k) == 0)) { keys[i] = y; keys[l] = x; }
+      }
+      __syncthreads();
+    }
+  const int32_t base = ws[AttnWs::head_base_off() / 4 + h];
+  int32_t* xq = ws + AttnWs::xq_off(nheads) / 4;
+  for (int i = threadIdx.x; i < nB; i += kPlanThreads)
+    xq[base + i] = (int32_t)(h * nB + (keys[i] & 2047u));
+}
+
+constexpr int kQT = 1;  // 32-query tiles per wave in the launched kernels
 
 template <int D, int BLK>
-fva_status launch_t(const Problem& p, const AttnArgs& a, int flags, bool dense, hipStream_t s) {
+fva_status launch_t(const Problem& p, AttnArgs a, int flags, bool dense, hipStream_t s) {
   const int sched = flags & 0x3;
   const bool trace = (flags & FVA_TRACE) != 0;
-  constexpr int NT = BLK * 4;
+  constexpr int NT = attn_threads<kQT>(BLK);
   if (dense) {
-    hipLaunchKernelGGL((attn_kernel<D, BLK, FVA_SCHED_GRID, true, false>), dim3((unsigned)p.rows),
+    hipLaunchKernelGGL((attn_kernel<D, BLK, kQT, FVA_SCHED_GRID, true, false>), dim3((unsigned)p.rows),
                        dim3(NT), 0, s, a);
     return hip_fail(hipGetLastError(), "dense attention launch");
   }
@@ -343,18 +537,27 @@ fva_status launch_t(const Problem& p, const AttnArgs& a, int flags, bool dense, 
   const int cus = device_cu_count();
   int per_cu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &per_cu, reinterpret_cast<const void*>(&attn_kernel<D, BLK, FVA_SCHED_QUEUE, false, false>),
+      &per_cu, reinterpret_cast<const void*>(&attn_kernel<D, BLK, kQT, FVA_SCHED_QUEUE, false, false>),
       NT, 0);
   if (e != hipSuccess) return hip_fail(e, "occupancy query");
   if (per_cu < 1) per_cu = 1;
   const int64_t persist = std::min<int64_t>(p.rows, (int64_t)cus * per_cu);
 #define FVA_LAUNCH(SCH, TR, GRIDN)                                                         \
-  hipLaunchKernelGGL((attn_kernel<D, BLK, SCH, false, TR>), dim3((unsigned)(GRIDN)), dim3(NT), \
+  hipLaunchKernelGGL((attn_kernel<D, BLK, kQT, SCH, false, TR>), dim3((unsigned)(GRIDN)), dim3(NT), \
                      0, s, a)
   if (sched == FVA_SCHED_QUEUE) {
-    hipLaunchKernelGGL(zero_counter, dim3(1), dim3(1), 0, s, a.counter);
+    hipLaunchKernelGGL(zero_counter, dim3(1), dim3(1), 0, s, a.ws);
     if (trace) FVA_LAUNCH(FVA_SCHED_QUEUE, true, persist);
     else FVA_LAUNCH(FVA_SCHED_QUEUE, false, persist);
+  } else if (sched == FVA_SCHED_XCD) {
+    const int nheads = p.B * p.Hh;
+    hipLaunchKernelGGL(xcd_assign_kernel, dim3(1), dim3(kPlanThreads), 0, s, a.head_count, nheads,
+                       p.nB, a.ws);
+    hipLaunchKernelGGL(xcd_fill_kernel, dim3(nheads), dim3(kPlanThreads), 0, s, a.row_count, p.nB,
+                       a.ws, (int64_t)nheads);
+    a.queue = a.ws + AttnWs::xq_off(nheads) / 4;
+    if (trace) FVA_LAUNCH(FVA_SCHED_XCD, true, persist);
+    else FVA_LAUNCH(FVA_SCHED_XCD, false, persist);
   } else if (sched == FVA_SCHED_STATIC) {
     if (trace) FVA_LAUNCH(FVA_SCHED_STATIC, true, persist);
     else FVA_LAUNCH(FVA_SCHED_STATIC, false, persist);
@@ -368,6 +571,8 @@ fva_status launch_t(const Problem& p, const AttnArgs& a, int flags, bool dense, 
 
 }  // namespace
 
+size_t attn_ws_bytes(const Problem& p) { return AttnWs::bytes((int64_t)p.B * p.Hh, p.rows); }
+
 fva_status launch_attn(const Problem& p, const void* qr, const void* kr, const void* vt,
                        void* out, const fva_mask* m, float scale, int flags, void* ws,
                        void* trace, bool dense, hipStream_t s) {
@@ -377,9 +582,10 @@ fva_status launch_attn(const Problem& p, const void* qr, const void* kr, const v
   a.vt = (const uint16_t*)vt;
   a.out = (uint16_t*)out;
   a.row_count = m ? m->row_count : nullptr;
+  a.head_count = m ? m->head_count : nullptr;
   a.col_idx = m ? m->col_idx : nullptr;
   a.queue = m ? m->queue : nullptr;
-  a.counter = (int32_t*)ws;
+  a.ws = (int32_t*)ws;
   a.trace = (uint32_t*)trace;
   a.N = p.N;
   a.Npad = p.Npad;

@@ -116,7 +116,7 @@ fva_status fva_sizes(const fva_grid* grid, int32_t B, int32_t Hh, int32_t d, fva
   out->words = p.words;
   out->rows = p.rows;
   out->route_ws_bytes = route_ws_layout(p).total;
-  out->attn_ws_bytes = kAttnWsBytes;
+  out->attn_ws_bytes = attn_ws_bytes(p);
   out->trace_bytes = (size_t)p.rows * 32;
   return FVA_OK;
 }
@@ -197,10 +197,14 @@ fva_status fva_sparse_attn(const void* qr, const void* kr, const void* vt, void*
   st = check_mask(mask, false);
   if (st != FVA_OK) return st;
   const int sched = flags & 0x3;
-  if ((flags & ~(0x3 | FVA_TRACE)) || sched == 0x3)
-    return fail(FVA_ERR_INVALID_ARG, "flags 0x%x", flags);
-  if (!ws || ws_bytes < kAttnWsBytes)
-    return fail(FVA_ERR_WORKSPACE, "attention workspace needs %zu bytes", kAttnWsBytes);
+  if (flags & ~(0x3 | FVA_TRACE)) return fail(FVA_ERR_INVALID_ARG, "flags 0x%x", flags);
+  if (sched == FVA_SCHED_XCD && (int64_t)B * Hh > kMaxXcdHeads)
+    return fail(FVA_ERR_UNSUPPORTED, "FVA_SCHED_XCD supports at most %d heads", kMaxXcdHeads);
+  const size_t need = attn_ws_bytes(p);
+  if (!ws || ws_bytes < need)
+    return fail(FVA_ERR_WORKSPACE, "attention workspace needs %zu bytes, got %zu", need,
+                ws ? ws_bytes : (size_t)0);
+  if (((uintptr_t)ws & 255u) != 0) return fail(FVA_ERR_WORKSPACE, "workspace not 256-byte aligned");
   if ((flags & FVA_TRACE) && !trace) return fail(FVA_ERR_INVALID_ARG, "FVA_TRACE needs a trace buffer");
   if (!(flags & FVA_TRACE)) trace = nullptr;
   if (!(scale > 0.f)) scale = 1.0f / sqrtf((float)d);

@@ -38,7 +38,9 @@ struct RouteWs {
   size_t total;
 };
 RouteWs route_ws_layout(const Problem& p);
-constexpr size_t kAttnWsBytes = 256;
+// Bytes of the attention workspace (scheduler counters and XCD row lists).
+size_t attn_ws_bytes(const Problem& p);
+constexpr int kMaxXcdHeads = 4096;
 
 // Kernel launchers (each returns FVA_OK or FVA_ERR_HIP).
 fva_status launch_reorder(const Problem& p, const void* src, void* dst, const int64_t st[3],

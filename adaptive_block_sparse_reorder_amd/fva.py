@@ -29,6 +29,7 @@ FVA_ROUTE_SCORES_IN = 0x1
 FVA_SCHED_QUEUE = 0x0
 FVA_SCHED_STATIC = 0x1
 FVA_SCHED_GRID = 0x2
+FVA_SCHED_XCD = 0x3
 FVA_TRACE = 0x10
 FVA_FORWARD = 0
 FVA_INVERSE = 1
@@ -244,7 +245,7 @@ def token_strides(x) -> Sequence[int]:
 
 
 def forward(buf: Buffers, q, k, v, top_p: float, topk_floor: int, aug_budget: int = 0,
-            scale: float = 0.0, route_flags: int = 0, attn_flags: int = FVA_SCHED_QUEUE,
+            scale: float = 0.0, route_flags: int = 0, attn_flags: int = FVA_SCHED_XCD,
             stream=None):
     """One pass of the hot path: reorder Q, K, V -> route -> block-sparse
     attention -> inverse reorder.  Inputs [B, N, Hh, d] bf16 on the device;

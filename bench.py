@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the adaptive block-sparse attention hot path on one MI355X.
+
+One step = the whole path on one synthetic batch already resident in HBM:
+reorder Q, K (rows layout) and V (vt64 layout) -> route (pool, scores, Top-p
+cut with Top-k floor, optional top-up, heaviest-first queue) -> block-sparse
+attention on the persistent queue -> inverse reorder of the output.
+
+Prints ONE JSON line.  `value` is executed attention TFLOP/s over whole steps
+(4*d*BLK^2 per selected block pair / step time).  `roofline` reports the
+sparse-attention kernel against the bf16 MFMA peak, its duration measured with
+HIP events on the stream it is launched on.  `cpu_baseline` times the float64
+CPU oracle on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 720p]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="720p")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip dense comparator and schedule traces (profiling runs)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--sched", default="xcd", choices=["queue", "static", "grid", "xcd"])
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def lambda_cu(trace_u32, rows):
+    """Per-CU busy time (sum of item durations) -> max/mean over CUs."""
+    import numpy as np
+    tr = trace_u32.reshape(-1, 8)[:rows]
+    t0 = tr[:, 4].astype(np.uint64) | (tr[:, 5].astype(np.uint64) << np.uint64(32))
+    t1 = tr[:, 6].astype(np.uint64) | (tr[:, 7].astype(np.uint64) << np.uint64(32))
+    dur = (t1 - t0).astype(np.float64)
+    xcc = tr[:, 1] & 0xF
+    hw = tr[:, 2]
+    cu_key = (xcc.astype(np.int64) << 16) | ((hw >> 8) & 0xFF).astype(np.int64)
+    keys, inv = np.unique(cu_key, return_inverse=True)
+    busy = np.bincount(inv, weights=dur)
+    span = float(t1.max() - t0.min())
+    return dict(lambda_cu=float(busy.max() / busy.mean()), cus=int(len(keys)),
+                busy_max_ms=float(busy.max()) / 1e5, busy_mean_ms=float(busy.mean()) / 1e5,
+                span_ms=span / 1e5)
+
+
+def cpu_baseline(w, q, k, v, seconds):
+    """Time the float64 oracle: its full routing, then its attention on a
+    seeded sample of (head, query-block) items until ~`seconds` elapse."""
+    import numpy as np
+    from oracle import fva_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    qr = O.reorder(q.float().numpy(), w.grid, w.block)
+    kr = O.reorder(k.float().numpy(), w.grid, w.block)
+    vr = O.reorder(v.float().numpy(), w.grid, w.block)
+    t1 = time.perf_counter()
+    r = O.route_path(qr, kr, w.N, w.BLK, w.scale, w.top_p, w.topk_floor, w.aug_budget)
+    t2 = time.perf_counter()
+    rng = np.random.default_rng(0)
+    items = rng.permutation(w.B * w.Hh * w.nB)
+    counts = r["counts"].reshape(-1)
+    flops, n = 0.0, 0
+    ts = time.perf_counter()
+    for it in items:
+        b, rem = divmod(int(it), w.Hh * w.nB)
+        h, i = divmod(rem, w.nB)
+        O.sparse_attention(qr, kr, vr, r["mask"], w.N, w.BLK, w.scale, items=[(b, h, i)])
+        flops += 4.0 * w.d * w.BLK * w.BLK * counts[it]
+        n += 1
+        if time.perf_counter() - ts >= seconds and n >= 4:
+            break
+    dt = time.perf_counter() - ts
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "sample": (f"float64 numpy oracle, attention of {n} seeded-random (head, query-block) "
+                   f"items of the {w.name} workload ({flops / 1e12:.3f} executed TFLOP in "
+                   f"{dt:.1f} s); its reorder of Q,K,V took {t1 - t0:.1f} s and routing of all "
+                   f"{w.B * w.Hh * w.nB} rows {t2 - t1:.1f} s (not in value)"),
+        "route_density": float(r["head_count"].sum() / (w.B * w.Hh * w.nB ** 2)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from adaptive_block_sparse_reorder_amd import fva as F
+    from adaptive_block_sparse_reorder_amd.inputs import WORKLOADS, make_qkv
+
+    args.sched = {"queue": F.FVA_SCHED_QUEUE, "static": F.FVA_SCHED_STATIC,
+                  "grid": F.FVA_SCHED_GRID, "xcd": F.FVA_SCHED_XCD}[args.sched]
+    sched_name = {v: k for k, v in {"queue": F.FVA_SCHED_QUEUE, "static": F.FVA_SCHED_STATIC,
+                  "grid": F.FVA_SCHED_GRID, "xcd": F.FVA_SCHED_XCD}.items()}[args.sched]
+    F.load_library()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    w = WORKLOADS[args.workload]
+    log(f"generating {w.name} inputs")
+    q, k, v = make_qkv(w)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    buf = F.alloc_buffers(w.grid, w.block, w.B, w.Hh, w.d, trace=True)
+    g = buf.grid
+    stream = torch.cuda.current_stream()
+    prm = F.fva_route_params(w.top_p, w.topk_floor, w.aug_budget, 0.0, 0)
+    m = buf.mask()
+
+    ev = {}
+
+    def mark(name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        ev.setdefault(name, []).append(e)
+
+    def step(timed):
+        if timed: mark("s0")
+        F.fva_reorder(qd, buf.qr, w.B, w.Hh, w.d, g, F.token_strides(qd))
+        F.fva_reorder(kd, buf.kr, w.B, w.Hh, w.d, g, F.token_strides(kd))
+        F.fva_reorder(vd, buf.vt, w.B, w.Hh, w.d, g, F.token_strides(vd), F.FVA_FORWARD,
+                      F.FVA_LAYOUT_VT64)
+        if timed: mark("s1")
+        F.fva_route(buf.qr, buf.kr, w.B, w.Hh, w.d, g, prm, m, buf.route_ws,
+                    buf.sizes.route_ws_bytes, 0)
+        if timed: mark("s2")
+        F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, g, m, 0.0,
+                          args.sched, buf.attn_ws, buf.sizes.attn_ws_bytes, None)
+        if timed: mark("s3")
+        F.fva_reorder(buf.orr, buf.out, w.B, w.Hh, w.d, g, F.token_strides(buf.out),
+                      F.FVA_INVERSE)
+        if timed: mark("s4")
+
+    log("warmup")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def avg(a, b):
+        return float(np.mean([x.elapsed_time(y) for x, y in zip(ev[a], ev[b])]))
+
+    ms_reorder, ms_route, ms_attn, ms_unre = (avg("s0", "s1"), avg("s1", "s2"),
+                                              avg("s2", "s3"), avg("s3", "s4"))
+    ms_step = wall * 1e3 / args.steps
+    nnz = int(buf.row_count.sum().item())
+    heads = buf.head_count.cpu().numpy().astype(np.float64) / (w.nB ** 2)
+    ex_flop = F.executed_flops(nnz, w.d, w.BLK)
+    de_flop = F.dense_equiv_flops(w.N, w.d, w.Hh, w.B)
+    attn_tflops = ex_flop / (ms_attn * 1e-3) / 1e12
+    # reorder: read N*Hh*d and write Npad*Hh*d bf16 for each of Q, K, V
+    reorder_bytes = 3 * 2 * w.B * w.Hh * w.d * (w.N + w.Npad)
+    unre_bytes = 2 * w.B * w.Hh * w.d * (w.N + w.N)
+
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step, attention {ms_attn:.3f} ms")
+    extras = {}
+    if not args.no_extras:
+        log("dense comparator and schedule traces")
+        # dense comparator, same core
+        for _ in range(2):
+            F.fva_dense_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, g)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        e0.record(stream)
+        for _ in range(reps):
+            F.fva_dense_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, g)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_dense = e0.elapsed_time(e1) / reps
+        extras["dense_ms"] = ms_dense
+        extras["dense_tflops"] = de_flop / (ms_dense * 1e-3) / 1e12
+        extras["speedup_vs_dense"] = ms_dense / ms_attn
+        # per-CU imbalance under the three schedules
+        lam = {}
+        for name, fl in (("static", F.FVA_SCHED_STATIC), ("grid", F.FVA_SCHED_GRID),
+                         ("queue", F.FVA_SCHED_QUEUE), ("xcd", F.FVA_SCHED_XCD)):
+            buf.trace.zero_()
+            F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, g, m, 0.0,
+                              fl | F.FVA_TRACE, buf.attn_ws, buf.sizes.attn_ws_bytes, buf.trace)
+            torch.cuda.synchronize()
+            lam[name] = lambda_cu(buf.trace.cpu().numpy().view(np.uint32), int(buf.sizes.rows))
+        extras["lambda_cu"] = lam
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu oracle baseline")
+        cpu = cpu_baseline(w, q, k, v, args.cpu_seconds)
+
+    out = {
+        "metric": "sparse-attn ms & executed TFLOP/s (% bf16 MFMA peak) at 720p Wan shape, 1 GPU",
+        "value": round(ex_flop / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: B={w.B} heads={w.Hh} d={w.d} grid={w.grid[0]}x{w.grid[1]}x"
+                        f"{w.grid[2]} ({w.N} tokens, {w.nB} blocks of {w.BLK}) block="
+                        f"{w.block[0]}x{w.block[1]}x{w.block[2]} top_p={w.top_p} "
+                        f"topk_floor={w.topk_floor} aug_budget={w.aug_budget}",
+            "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "mfma", "kernel": f"attn_kernel (sparse, {sched_name} schedule)",
+            "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+        },
+        "cpu_baseline": cpu,
+        "breakdown": {
+            "sparse_attn_ms": round(ms_attn, 4),
+            "executed_tflop": round(ex_flop / 1e12, 3),
+            "dense_equiv_tflop": round(de_flop / 1e12, 3),
+            "executed_tflops": round(attn_tflops, 2),
+            "dense_equiv_tflops": round(de_flop / (ms_attn * 1e-3) / 1e12, 2),
+            "density": {"mean": float(heads.mean()), "min": float(heads.min()),
+                        "max": float(heads.max())},
+            "reorder_qkv_ms": round(ms_reorder, 4),
+            "reorder_qkv_GBs": round(reorder_bytes / (ms_reorder * 1e-3) / 1e9, 1),
+            "route_ms": round(ms_route, 4),
+            "unreorder_ms": round(ms_unre, 4),
+            "unreorder_GBs": round(unre_bytes / (ms_unre * 1e-3) / 1e9, 1),
+            **{k2: (round(v2, 4) if isinstance(v2, float) else v2) for k2, v2 in extras.items()},
+        },
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -112,6 +112,11 @@ typedef struct {
                                  rows in row order (fixed placement)         */
 #define FVA_SCHED_GRID   0x2  /* one workgroup per queue entry, hardware
                                  dispatch                                    */
+#define FVA_SCHED_XCD    0x3  /* persistent, XCD-aware: heads assigned to the
+                                 8 XCDs by longest-processing-time on W_h;
+                                 each XCD pops its heads' rows heaviest first
+                                 and steals from the others when it runs dry
+                                 (at most 4096 heads)                        */
 #define FVA_TRACE        0x10 /* write one trace record per item             */
 
 /* fva_reorder directions and layouts */
@@ -177,7 +182,8 @@ fva_status fva_route_flags(const void* ws, uint32_t* flags_out, hipStream_t stre
  * softmax.  Rows with no selected block, and pad rows, are written as zero.
  * qr, kr: `rows` bf16; vt: `vt64` bf16; out: `rows` bf16.
  * scale <= 0 selects 1/sqrt(d).  flags: one FVA_SCHED_* value, optionally
- * | FVA_TRACE.  ws: fva_sizes().attn_ws_bytes bytes (scheduler counter).
+ * | FVA_TRACE.  ws: fva_sizes().attn_ws_bytes bytes, 256-byte aligned
+ * (scheduler counters and lists; contents need not be initialized).
  * trace (with FVA_TRACE): trace_bytes bytes; record k (8 x uint32) describes
  * the k-th processed queue entry: {row, XCC_ID, HW_ID, workgroup id,
  * t0 lo, t0 hi, t1 lo, t1 hi} with t = s_memrealtime ticks (100 MHz).     */

@@ -37,6 +37,7 @@ def test_sizes_match_workloads(lib, name, N, Npad, nB, words):
     assert (s.N, s.Npad, s.nB, s.words, s.BLK) == (N, Npad, nB, words, w.BLK)
     assert s.rows == w.B * w.Hh * nB
     assert s.trace_bytes == 32 * s.rows
+    assert s.attn_ws_bytes >= 256 + 4 * s.rows + 4 * w.Hh
     # route workspace: status word + pooled q, k (float32) + per-head thresholds
     assert s.route_ws_bytes >= 256 + 2 * 4 * s.rows * w.d + 8 * w.Hh
 
@@ -82,12 +83,20 @@ def test_validation_errors_before_launch(lib):
     assert lib.fva_route(16, 16, 1, 2, 64, ctypes.byref(g), ctypes.byref(prm), ctypes.byref(m0),
                          256, 1 << 30, 0, None) == F.FVA_ERR_INVALID_ARG
     # attention: bad schedule flag, missing workspace, trace without buffer
+    big_ws = 1 << 20
     assert lib.fva_sparse_attn(16, 16, 16, 16, 1, 2, 64, ctypes.byref(g), ctypes.byref(m), 0.0,
-                               0x3, 256, 256, None, None) == F.FVA_ERR_INVALID_ARG
+                               0x4, 256, big_ws, None, None) == F.FVA_ERR_INVALID_ARG
     assert lib.fva_sparse_attn(16, 16, 16, 16, 1, 2, 64, ctypes.byref(g), ctypes.byref(m), 0.0,
                                0, None, 0, None, None) == F.FVA_ERR_WORKSPACE
     assert lib.fva_sparse_attn(16, 16, 16, 16, 1, 2, 64, ctypes.byref(g), ctypes.byref(m), 0.0,
-                               F.FVA_TRACE, 256, 256, None, None) == F.FVA_ERR_INVALID_ARG
+                               0, 256, 64, None, None) == F.FVA_ERR_WORKSPACE
+    assert lib.fva_sparse_attn(16, 16, 16, 16, 1, 2, 64, ctypes.byref(g), ctypes.byref(m), 0.0,
+                               F.FVA_TRACE, 256, big_ws, None, None) == F.FVA_ERR_INVALID_ARG
+    # the XCD schedule caps the number of heads
+    many = F.make_grid((2, 8, 8), (1, 8, 8))
+    assert lib.fva_sparse_attn(256, 256, 256, 256, 1, 5000, 64, ctypes.byref(many),
+                               ctypes.byref(m), 0.0, F.FVA_SCHED_XCD, 256, 1 << 30, None,
+                               None) == F.FVA_ERR_UNSUPPORTED
     assert lib.fva_dense_attn(16, 16, 0, 16, 1, 2, 64, ctypes.byref(g), 0.0, None) == \
         F.FVA_ERR_INVALID_ARG
     assert lib.fva_status_string(F.FVA_ERR_WORKSPACE) == b"FVA_ERR_WORKSPACE"

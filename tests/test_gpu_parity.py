@@ -260,7 +260,7 @@ def test_sparse_attention_matches_oracle(entry):
     check_mask_exact(buf, r, w.nB)
     ref = _oracle_attention(w, q, k, v, r["mask"])
     outs = {}
-    for fl in (F.FVA_SCHED_QUEUE, F.FVA_SCHED_STATIC, F.FVA_SCHED_GRID):
+    for fl in (F.FVA_SCHED_QUEUE, F.FVA_SCHED_STATIC, F.FVA_SCHED_GRID, F.FVA_SCHED_XCD):
         buf.orr.fill_(float("nan"))
         attn(buf, fl)
         torch.cuda.synchronize()
@@ -271,7 +271,7 @@ def test_sparse_attention_matches_oracle(entry):
     assert mx <= MAX_ABS and rel <= MEAN_REL
     assert np.all(got[:, :, w.N:] == 0)
     # every schedule computes every row identically
-    for fl in (F.FVA_SCHED_STATIC, F.FVA_SCHED_GRID):
+    for fl in (F.FVA_SCHED_STATIC, F.FVA_SCHED_GRID, F.FVA_SCHED_XCD):
         assert torch.equal(outs[fl].view(torch.int16), outs[F.FVA_SCHED_QUEUE].view(torch.int16))
 
 
@@ -324,7 +324,7 @@ def test_trace_covers_every_item_once():
     q, k, v, qd, kd, vd, buf = setup(w)
     gpu_reorder(buf, qd, kd, vd)
     route(buf, w)
-    for fl in (F.FVA_SCHED_QUEUE, F.FVA_SCHED_STATIC, F.FVA_SCHED_GRID):
+    for fl in (F.FVA_SCHED_QUEUE, F.FVA_SCHED_STATIC, F.FVA_SCHED_GRID, F.FVA_SCHED_XCD):
         buf.trace.zero_()
         attn(buf, fl | F.FVA_TRACE)
         torch.cuda.synchronize()
