@@ -43,7 +43,30 @@ def parse():
                     help="skip dense comparator and schedule traces (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--sched", default="xcd", choices=["queue", "static", "grid", "xcd"])
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed steps, run one plain device copy of this many MiB "
+                         "(reference kernel for HBM byte counters)")
     return ap.parse_args()
+
+
+def measured_traffic(workload, sched_name):
+    """HBM bytes per launch of the sparse kernel from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary, when it was taken on this workload and
+    schedule with the current kernel source; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"attn_kernel_{workload}_hbm_traffic.txt")
+    src = os.path.join(ROOT, "adaptive_block_sparse_reorder_amd", "csrc", "attn.hip")
+    if sched_name != "xcd" or not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip().split()[0] if v.strip() else ""
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if kv.get("attn_source_sha256_16") != sha:
+        return None
+    return float(kv["attn_hbm_bytes"])
 
 
 def log(msg):
@@ -187,6 +210,14 @@ def main():
     unre_bytes = 2 * w.B * w.Hh * w.d * (w.N + w.N)
 
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step, attention {ms_attn:.3f} ms")
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     extras = {}
     if not args.no_extras:
         log("dense comparator and schedule traces")
@@ -243,7 +274,8 @@ def main():
         "roofline": {
             "bound": "mfma", "kernel": f"attn_kernel (sparse, {sched_name} schedule)",
             "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic(w.name, sched_name),
         },
         "cpu_baseline": cpu,
         "breakdown": {
