@@ -61,13 +61,12 @@ __device__ __forceinline__ void g2lds16(const void* g, char* lds_uniform) {
                                    0);
 }
 
-// K sub-tile: 64 rows (keys) x D bf16; 16-byte chunk c of row r lives at
-// physical chunk c ^ swz(r).  V^T sub-tile: D rows (channels) x 64 slots.
-template <int D>
-__device__ __forceinline__ int swz_k(int r) {
-  return D == 128 ? (r & 15) : ((r >> 1) & 7);
-}
-__device__ __forceinline__ int swz_v(int r) { return (r >> 1) & 7; }
+// LDS tiles are verbatim copies of the k64 / v64 HBM tiles:
+//   K tile: 16-byte unit (c, r) = channels 8c..8c+7 of key r at byte (c*64 + r)*16
+//   V tile: 16-byte unit (g, e) = channel e of key slots 8g..8g+7 at byte (g*D + e)*16
+// A wave's MFMA operand read touches 64 consecutive units (one lane each), so
+// every read is conflict-free and its address is one per-lane base plus an
+// immediate offset.
 
 // Attention workspace: [0,256) counters and per-XCD offsets, then per-head
 // bases, then the XCD-ordered row list.
@@ -129,20 +128,9 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_
   const int l32 = lane & 31;
   const int hl = lane >> 5;
 
-  // per-thread element offsets of its 16-byte loads inside a K and a V^T tile
-  int koff[LOADS], voff[LOADS];
-#pragma unroll
-  for (int k = 0; k < LOADS; ++k) {
-    const int slot = (k * NW + wave) * 64 + lane;
-    {
-      const int r = slot / CPR, p = slot % CPR;
-      koff[k] = r * D + ((p ^ swz_k<D>(r)) * 8);
-    }
-    {
-      const int r = slot / 8, p = slot % 8;
-      voff[k] = r * KT + ((p ^ swz_v(r)) * 8);
-    }
-  }
+  // byte offset of this thread's first 16-byte load inside a tile; load k of
+  // the wave adds k*NW*1024 (each wave instruction moves 1 KB contiguously)
+  const uint32_t loff = (uint32_t)(wave * 64 + lane) * 16u;
 
   const int xcd = blockIdx.x % NXCD;
   int victim = 0;  // XCD schedule: how far thread 0 has moved from its own XCD
@@ -217,25 +205,21 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_
     U = __builtin_amdgcn_readfirstlane(U);
 
     const uint16_t* kbase = a.kr + bh * a.Npad * D;
-    const uint16_t* vbase = a.vt + bh * a.Npad * D;  // vt64 chunk of key0 at key0*D
+    const uint16_t* vbase = a.vt + bh * a.Npad * D;  // tiles of key0 start at key0*D
 
     auto key0_of = [&](int u) -> int64_t {
       const int t = u / NSUB, half = u % NSUB;
       const int kb = DENSE ? t : __builtin_amdgcn_readfirstlane((int)s_cols[t]);
       return (int64_t)kb * BLK + half * KT;
     };
-    auto load_k = [&](int u) {
-      char* buf = lds + (u & 1) * TILE;
-      const uint16_t* src = kbase + key0_of(u) * D;
+    auto load_tile = [&](const uint16_t* base, int u, char* buf) {
+      const char* src = (const char*)(base + key0_of(u) * D) + loff;
 #pragma unroll
-      for (int k = 0; k < LOADS; ++k) g2lds16(src + koff[k], buf + (k * NW + wave) * 1024);
+      for (int k = 0; k < LOADS; ++k)
+        g2lds16(src + k * NW * 1024, buf + (k * NW + wave) * 1024);
     };
-    auto load_v = [&](int u) {
-      char* buf = lds + (2 + (u & 1)) * TILE;
-      const uint16_t* src = vbase + key0_of(u) * D;
-#pragma unroll
-      for (int k = 0; k < LOADS; ++k) g2lds16(src + voff[k], buf + (k * NW + wave) * 1024);
-    };
+    auto load_k = [&](int u) { load_tile(kbase, u, lds + (u & 1) * TILE); };
+    auto load_v = [&](int u) { load_tile(vbase, u, lds + (2 + (u & 1)) * TILE); };
 
     // Q^T operands: q-tile j of this wave = 32 queries; lane holds query l32, d chunk 2kk+hl
     const int64_t q0 = (int64_t)qb * BLK + wave * 32 * QT;
@@ -267,11 +251,10 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_
         for (int j = 0; j < QT; ++j)
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[m][j][r] = 0.f;
-        const int kr_ = 32 * m + l32;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-          const int c = (2 * kk + hl) ^ swz_k<D>(kr_);
-          const bf16x8 kop = as_bf16x8(*(const u32x4*)(kt + kr_ * (D * 2) + c * 16));
+          const bf16x8 kop = as_bf16x8(
+              *(const u32x4*)(kt + (2 * kk + hl) * 1024 + (32 * m + l32) * 16));
 #pragma unroll
           for (int j = 0; j < QT; ++j)
             s[m][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[j][kk], s[m][j], 0, 0, 0);
@@ -350,13 +333,12 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_
       const char* vtile = lds + (2 + (u & 1)) * TILE;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int vr = 32 * dt + l32;
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
-            const int c = (4 * m + 2 * b + hl) ^ swz_v(vr);
-            const bf16x8 vop = as_bf16x8(*(const u32x4*)(vtile + vr * (KT * 2) + c * 16));
+            const bf16x8 vop = as_bf16x8(*(const u32x4*)(
+                vtile + (4 * m + 2 * b + hl) * (D * 16) + (32 * dt + l32) * 16));
 #pragma unroll
             for (int j = 0; j < QT; ++j)
               oacc[dt][j] =

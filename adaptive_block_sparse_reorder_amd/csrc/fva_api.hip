@@ -130,7 +130,7 @@ fva_status fva_reorder(const void* src, void* dst, int32_t B, int32_t Hh, int32_
   if (!src || !dst || !strides) return fail(FVA_ERR_INVALID_ARG, "null pointer");
   if (direction != FVA_FORWARD && direction != FVA_INVERSE)
     return fail(FVA_ERR_INVALID_ARG, "direction %d", direction);
-  if (layout != FVA_LAYOUT_ROWS && layout != FVA_LAYOUT_VT64)
+  if (layout != FVA_LAYOUT_ROWS && layout != FVA_LAYOUT_V64 && layout != FVA_LAYOUT_K64)
     return fail(FVA_ERR_INVALID_ARG, "layout %d", layout);
   if (direction == FVA_INVERSE && layout != FVA_LAYOUT_ROWS)
     return fail(FVA_ERR_INVALID_ARG, "inverse reorder writes the token-major layout only");

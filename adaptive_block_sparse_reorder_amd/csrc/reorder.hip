@@ -8,9 +8,8 @@
 // (all heads of a token are adjacent in the source) and writes whole 2*d-byte
 // destination rows.
 //
-// Forward vt64: each workgroup owns one 64-token chunk of one head; rows are
-// staged in LDS and written transposed (d-major, 128 contiguous bytes per
-// channel), with the token slot's bits 2 and 3 swapped.
+// Forward k64 / v64: each workgroup owns one 64-token chunk of one head and
+// writes it in the tile layout the attention kernel stages into LDS verbatim.
 #include "fva_internal.hpp"
 
 namespace fva {
@@ -74,18 +73,23 @@ __global__ __launch_bounds__(kThreads) void reorder_rows_inv(
   }
 }
 
-// slot of token offset k inside a 64-token vt64 chunk: bits 2 and 3 swapped
-__device__ __forceinline__ int vt_slot(int k) {
+// slot of token offset k inside a 64-token V chunk: bits 2 and 3 swapped
+__device__ __forceinline__ int v_slot(int k) {
   return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void reorder_vt64_fwd(
+// Forward into one of the 64-token tile layouts.  The workgroup stages the
+// chunk's 64 token rows of one head in LDS (rows padded by 16 bytes so the
+// 16-byte column reads below are free of bank conflicts), then writes the
+// 16 KB (d=128) tile in one contiguous, coalesced sweep.
+//   K64: unit (c, r) = channels 8c..8c+7 of token r, at unit index c*64 + r
+//   V64: unit (g, e) = channel e of the tokens in slots 8g..8g+7, at g*D + e
+template <int D, bool IS_V>
+__global__ __launch_bounds__(kThreads) void reorder_tile64_fwd(
     const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, BlockOrder bo, int64_t N,
     int64_t Npad, int Hh, int64_t sb, int64_t sn, int64_t sh) {
-  // stage[k][c], row padded by one 16-byte chunk against bank conflicts
   constexpr int kPitch = D + 8;
-  __shared__ uint16_t stage[64 * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t stage[64 * kPitch];
   __shared__ int64_t tok[64];
   const int64_t chunk = blockIdx.x;  // 64-token chunk index within the head
   const int bh = blockIdx.y;
@@ -105,24 +109,23 @@ __global__ __launch_bounds__(kThreads) void reorder_vt64_fwd(
     *(u32x4*)(&stage[k * kPitch + c * 8]) = v;
   }
   __syncthreads();
-  // output: D rows (channels) x 64 slots; each thread writes 8 slots (16 B)
-  uint16_t* out = dst + ((int64_t)bh * (Npad / 64) + chunk) * (int64_t)D * 64;
-  for (int L = threadIdx.x; L < D * 8; L += kThreads) {
-    const int sg = L % 8;    // slot group of 8
-    const int c = L / 8;     // channel
-    uint16_t vals[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int slot = sg * 8 + e;
-      const int k = vt_slot(slot);  // the swap is an involution
-      vals[e] = stage[k * kPitch + c];
-    }
+  u32x4* out = (u32x4*)(dst + ((int64_t)bh * (Npad / 64) + chunk) * (int64_t)D * 64);
+  for (int u = threadIdx.x; u < 64 * cpr; u += kThreads) {
     u32x4 v;
-    v.x = vals[0] | ((uint32_t)vals[1] << 16);
-    v.y = vals[2] | ((uint32_t)vals[3] << 16);
-    v.z = vals[4] | ((uint32_t)vals[5] << 16);
-    v.w = vals[6] | ((uint32_t)vals[7] << 16);
-    *(u32x4*)(out + c * 64 + sg * 8) = v;
+    if (!IS_V) {
+      const int c = u / 64, r = u % 64;
+      v = *(const u32x4*)(&stage[r * kPitch + c * 8]);
+    } else {
+      const int g = u / D, e = u % D;
+      uint16_t vals[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) vals[q] = stage[v_slot(8 * g + q) * kPitch + e];
+      v.x = vals[0] | ((uint32_t)vals[1] << 16);
+      v.y = vals[2] | ((uint32_t)vals[3] << 16);
+      v.z = vals[4] | ((uint32_t)vals[5] << 16);
+      v.w = vals[6] | ((uint32_t)vals[7] << 16);
+    }
+    out[u] = v;
   }
 }
 
@@ -143,12 +146,18 @@ fva_status launch_reorder(const Problem& p, const void* src, void* dst, const in
                        p.Hh, p.d, st[0], st[1], st[2]);
   } else {
     dim3 grid((unsigned)(p.Npad / 64), (unsigned)(p.B * p.Hh));
-    if (p.d == 128)
-      hipLaunchKernelGGL(reorder_vt64_fwd<128>, grid, dim3(kThreads), 0, s, in, out, bo, p.N,
-                         p.Npad, p.Hh, st[0], st[1], st[2]);
-    else
-      hipLaunchKernelGGL(reorder_vt64_fwd<64>, grid, dim3(kThreads), 0, s, in, out, bo, p.N,
-                         p.Npad, p.Hh, st[0], st[1], st[2]);
+    const bool v = layout == FVA_LAYOUT_V64;
+#define FVA_TILE_LAUNCH(DD, VV)                                                               \
+  hipLaunchKernelGGL((reorder_tile64_fwd<DD, VV>), grid, dim3(kThreads), 0, s, in, out, bo, p.N, \
+                     p.Npad, p.Hh, st[0], st[1], st[2])
+    if (p.d == 128) {
+      if (v) FVA_TILE_LAUNCH(128, true);
+      else FVA_TILE_LAUNCH(128, false);
+    } else {
+      if (v) FVA_TILE_LAUNCH(64, true);
+      else FVA_TILE_LAUNCH(64, false);
+    }
+#undef FVA_TILE_LAUNCH
   }
   return hip_fail(hipGetLastError(), "reorder launch");
 }

@@ -34,7 +34,8 @@ FVA_TRACE = 0x10
 FVA_FORWARD = 0
 FVA_INVERSE = 1
 FVA_LAYOUT_ROWS = 0
-FVA_LAYOUT_VT64 = 1
+FVA_LAYOUT_V64 = 1
+FVA_LAYOUT_K64 = 2
 
 
 class fva_grid(ctypes.Structure):
@@ -228,8 +229,8 @@ def alloc_buffers(grid: Sequence[int], block: Sequence[int], B: int, Hh: int, d:
 
     return Buffers(
         grid=g, sizes=sz, B=B, Hh=Hh, d=d,
-        qr=dev((B, Hh, sz.Npad, d), bf), kr=dev((B, Hh, sz.Npad, d), bf),
-        vt=dev((B, Hh, sz.Npad // 64, d, 64), bf), orr=dev((B, Hh, sz.Npad, d), bf),
+        qr=dev((B, Hh, sz.Npad, d), bf), kr=dev((B, Hh, sz.Npad // 64, d // 8, 64, 8), bf),
+        vt=dev((B, Hh, sz.Npad // 64, 8, d, 8), bf), orr=dev((B, Hh, sz.Npad, d), bf),
         out=dev((B, int(sz.N), Hh, d), bf),
         scores=dev((rows, nB), torch.float32), bitmask=dev((rows, int(sz.words)), torch.int32),
         row_count=dev((rows,), torch.int32), col_idx=dev((rows, nB), torch.int16),
@@ -247,13 +248,13 @@ def token_strides(x) -> Sequence[int]:
 def forward(buf: Buffers, q, k, v, top_p: float, topk_floor: int, aug_budget: int = 0,
             scale: float = 0.0, route_flags: int = 0, attn_flags: int = FVA_SCHED_XCD,
             stream=None):
-    """One pass of the hot path: reorder Q, K, V -> route -> block-sparse
+    """One pass of the hot path: reorder Q (rows), K (k64), V (v64) -> route -> block-sparse
     attention -> inverse reorder.  Inputs [B, N, Hh, d] bf16 on the device;
     the result lands in buf.out."""
     g, B, Hh, d = buf.grid, buf.B, buf.Hh, buf.d
     fva_reorder(q, buf.qr, B, Hh, d, g, token_strides(q), FVA_FORWARD, FVA_LAYOUT_ROWS, stream)
-    fva_reorder(k, buf.kr, B, Hh, d, g, token_strides(k), FVA_FORWARD, FVA_LAYOUT_ROWS, stream)
-    fva_reorder(v, buf.vt, B, Hh, d, g, token_strides(v), FVA_FORWARD, FVA_LAYOUT_VT64, stream)
+    fva_reorder(k, buf.kr, B, Hh, d, g, token_strides(k), FVA_FORWARD, FVA_LAYOUT_K64, stream)
+    fva_reorder(v, buf.vt, B, Hh, d, g, token_strides(v), FVA_FORWARD, FVA_LAYOUT_V64, stream)
     prm = fva_route_params(top_p, topk_floor, aug_budget, scale, 0)
     m = buf.mask()
     fva_route(buf.qr, buf.kr, B, Hh, d, g, prm, m, buf.route_ws, buf.sizes.route_ws_bytes,

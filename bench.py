@@ -2,7 +2,7 @@
 """Benchmark of the adaptive block-sparse attention hot path on one MI355X.
 
 One step = the whole path on one synthetic batch already resident in HBM:
-reorder Q, K (rows layout) and V (vt64 layout) -> route (pool, scores, Top-p
+reorder Q (rows layout), K (k64 tiles) and V (v64 tiles) -> route (pool, scores, Top-p
 cut with Top-k floor, optional top-up, heaviest-first queue) -> block-sparse
 attention on the persistent queue -> inverse reorder of the output.
 
@@ -170,9 +170,10 @@ def main():
     def step(timed):
         if timed: mark("s0")
         F.fva_reorder(qd, buf.qr, w.B, w.Hh, w.d, g, F.token_strides(qd))
-        F.fva_reorder(kd, buf.kr, w.B, w.Hh, w.d, g, F.token_strides(kd))
+        F.fva_reorder(kd, buf.kr, w.B, w.Hh, w.d, g, F.token_strides(kd), F.FVA_FORWARD,
+                      F.FVA_LAYOUT_K64)
         F.fva_reorder(vd, buf.vt, w.B, w.Hh, w.d, g, F.token_strides(vd), F.FVA_FORWARD,
-                      F.FVA_LAYOUT_VT64)
+                      F.FVA_LAYOUT_V64)
         if timed: mark("s1")
         F.fva_route(buf.qr, buf.kr, w.B, w.Hh, w.d, g, prm, m, buf.route_ws,
                     buf.sizes.route_ws_bytes, 0)

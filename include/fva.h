@@ -34,10 +34,13 @@
  * Npad = nB*BLK):
  *   token-major   [B, N, Hh, d]  the DiT layout, element strides given by caller
  *   rows          [B, Hh, Npad, d] reordered, contiguous, pad rows zero
- *   vt64          [B, Hh, Npad/64, d, 64] reordered V, each chunk of 64
- *                 consecutive reordered tokens stored d-major; inside a chunk
- *                 the token slot is the token offset with bits 2 and 3
- *                 swapped (a layout chosen for the MFMA operand order).
+ *   k64           [B, Hh, Npad/64, d/8, 64, 8] reordered K in 64-token tiles:
+ *                 element (c, r, e) of tile t is channel 8c+e of token 64t+r
+ *   v64           [B, Hh, Npad/64, 8, d, 8] reordered V in 64-token tiles:
+ *                 element (g, e, q) of tile t is channel e of token 64t+k
+ *                 where k is slot 8g+q with bits 2 and 3 swapped
+ *   (the tile layouts are the order in which the attention kernel's MFMA
+ *   operands are read, so a tile is copied to LDS verbatim; pad tokens zero)
  */
 #ifndef FVA_H
 #define FVA_H
@@ -123,7 +126,8 @@ typedef struct {
 #define FVA_FORWARD 0
 #define FVA_INVERSE 1
 #define FVA_LAYOUT_ROWS 0
-#define FVA_LAYOUT_VT64 1
+#define FVA_LAYOUT_V64 1
+#define FVA_LAYOUT_K64 2
 
 /* Sizes of a problem and the workspaces it needs.  B, Hh > 0; d as above.
  * Returns FVA_ERR_UNSUPPORTED for shapes outside the supported set.        */
@@ -137,8 +141,8 @@ fva_status fva_sizes(const fva_grid* grid, int32_t B, int32_t Hh, int32_t d,
  *
  * FVA_FORWARD: src is token-major [B, N, Hh, d] with element strides
  *   strides[0..2] for (b, n, h) and unit channel stride; dst is `rows`
- *   (layout FVA_LAYOUT_ROWS, pad rows written as zero) or `vt64`
- *   (FVA_LAYOUT_VT64, pad tokens zero).
+ *   (FVA_LAYOUT_ROWS), `k64` (FVA_LAYOUT_K64) or `v64` (FVA_LAYOUT_V64);
+ *   pad tokens are written as zero.
  * FVA_INVERSE: src is `rows`; dst is token-major [B, N, Hh, d] with element
  *   strides strides[0..2]; pad rows are dropped.  Layout must be ROWS.
  * Pointers and strides must be 16-byte aligned (strides multiples of 8).
@@ -148,7 +152,7 @@ fva_status fva_reorder(const void* src, void* dst, int32_t B, int32_t Hh, int32_
                        int32_t direction, int32_t layout, hipStream_t stream);
 
 /* Sparse-routing frontend (sections 2 and 3.1; top-up section 3.3).
- * qr, kr: `rows` layout bf16.  For every row (b, h, i):
+ * qr: `rows` bf16, kr: `k64` bf16.  For every row (b, h, i):
  *   1. unless FVA_ROUTE_SCORES_IN: qbar, kbar = mean of each block's real
  *      tokens; scores[r, j] = (qbar_i . kbar_j) * scale in float32;
  *   2. importance order = key blocks by score descending, ties by index
@@ -180,7 +184,7 @@ fva_status fva_route_flags(const void* ws, uint32_t* flags_out, hipStream_t stre
  *         softmax_k((q . k) * scale) * v_k,
  * computed with bf16 MFMA products, float32 accumulation and an online
  * softmax.  Rows with no selected block, and pad rows, are written as zero.
- * qr, kr: `rows` bf16; vt: `vt64` bf16; out: `rows` bf16.
+ * qr: `rows` bf16; kr: `k64` bf16; vt: `v64` bf16; out: `rows` bf16.
  * scale <= 0 selects 1/sqrt(d).  flags: one FVA_SCHED_* value, optionally
  * | FVA_TRACE.  ws: fva_sizes().attn_ws_bytes bytes, 256-byte aligned
  * (scheduler counters and lists; contents need not be initialized).

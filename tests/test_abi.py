@@ -66,7 +66,7 @@ def test_validation_errors_before_launch(lib):
     st2 = (ctypes.c_int64 * 3)(1280 * 2 * 64, 2 * 64, 63)
     assert lib.fva_reorder(16, 32, 1, 2, 64, ctypes.byref(g), st2, 0, 0, None) == \
         F.FVA_ERR_INVALID_ARG
-    # inverse into the vt64 layout is not a thing
+    # the inverse writes the token-major layout only
     assert lib.fva_reorder(16, 32, 1, 2, 64, ctypes.byref(g), st, 1, 1, None) == \
         F.FVA_ERR_INVALID_ARG
     # route: workspace too small, negative floor, bad flags

@@ -65,14 +65,23 @@ def unpack_bitmask(bm, nB):
     return out
 
 
-def vt64_expected(rows):
-    """Oracle reordered V [B, Hh, Npad, d] -> vt64 layout by the header's
-    definition: chunk c, channel e, slot s holds token c*64 + swap23(s)."""
+def k64_expected(rows):
+    """Oracle reordered K [B, Hh, Npad, d] -> k64 tiles by the header's
+    definition: tile t, unit (c, r), element e = channel 8c+e of token 64t+r."""
+    B, Hh, Npad, d = rows.shape
+    x = rows.reshape(B, Hh, Npad // 64, 64, d // 8, 8)          # t, r, c, e
+    return np.ascontiguousarray(np.transpose(x, (0, 1, 2, 4, 3, 5)))  # t, c, r, e
+
+
+def v64_expected(rows):
+    """Oracle reordered V -> v64 tiles: tile t, unit (g, e), element q =
+    channel e of token 64t + k, k = slot 8g+q with bits 2 and 3 swapped."""
     B, Hh, Npad, d = rows.shape
     s = np.arange(64)
-    sw = (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1)
-    x = rows.reshape(B, Hh, Npad // 64, 64, d)[:, :, :, sw, :]
-    return np.ascontiguousarray(np.swapaxes(x, 3, 4))
+    k = (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1)
+    x = rows.reshape(B, Hh, Npad // 64, 64, d)[:, :, :, k, :]   # t, slot, e
+    x = x.reshape(B, Hh, Npad // 64, 8, 8, d)                   # t, g, q, e
+    return np.ascontiguousarray(np.transpose(x, (0, 1, 2, 3, 5, 4)))  # t, g, e, q
 
 
 def err_stats(got, ref):
@@ -90,9 +99,10 @@ def setup(w, seed=None):
 def gpu_reorder(buf, qd, kd, vd):
     g = buf.grid
     F.fva_reorder(qd, buf.qr, buf.B, buf.Hh, buf.d, g, F.token_strides(qd))
-    F.fva_reorder(kd, buf.kr, buf.B, buf.Hh, buf.d, g, F.token_strides(kd))
+    F.fva_reorder(kd, buf.kr, buf.B, buf.Hh, buf.d, g, F.token_strides(kd), F.FVA_FORWARD,
+                  F.FVA_LAYOUT_K64)
     F.fva_reorder(vd, buf.vt, buf.B, buf.Hh, buf.d, g, F.token_strides(vd), F.FVA_FORWARD,
-                  F.FVA_LAYOUT_VT64)
+                  F.FVA_LAYOUT_V64)
 
 
 def route(buf, w, scores_in=None, top_p=None, topk=None, aug=None):
@@ -135,10 +145,11 @@ def test_reorder_bit_exact(entry):
     q, k, v, qd, kd, vd, buf = setup(w)
     gpu_reorder(buf, qd, kd, vd)
     torch.cuda.synchronize()
-    for x, dev in ((q, buf.qr), (k, buf.kr)):
-        ref = O.reorder(x.view(torch.int16).numpy(), w.grid, w.block)
-        assert np.array_equal(bits(dev), ref)
-    vref = vt64_expected(O.reorder(v.view(torch.int16).numpy(), w.grid, w.block))
+    qref = O.reorder(q.view(torch.int16).numpy(), w.grid, w.block)
+    assert np.array_equal(bits(buf.qr), qref)
+    kref = k64_expected(O.reorder(k.view(torch.int16).numpy(), w.grid, w.block))
+    assert np.array_equal(bits(buf.kr), kref)
+    vref = v64_expected(O.reorder(v.view(torch.int16).numpy(), w.grid, w.block))
     assert np.array_equal(bits(buf.vt), vref)
     # inverse of the reordered Q gives Q back
     out = torch.empty_like(qd)
