@@ -26,11 +26,11 @@
 //
 // Schedules: static contiguous split (fixed placement), hardware grid over the
 // heaviest-first queue, a persistent atomic heaviest-first queue, and an
-// XCD-aware persistent schedule: heads are assigned to the 8 XCDs by
-// longest-processing-time on their realized workload W_h, each XCD walks its
-// heads' rows heaviest first (rows of one head stay together so their K/V
-// stream through that XCD's L2), and a workgroup whose XCD runs dry steals
-// from the other XCDs' queues.
+// XCD-aware persistent schedule: heads are placed on the 8 XCDs heaviest
+// first by longest-processing-time on their realized workload W_h, each XCD
+// walks its heads' rows in query-block order (neighbouring query blocks share
+// most key blocks, so their K/V stream through that XCD's L2 once), and a
+// workgroup whose XCD runs dry steals from the other XCDs' lists.
 #include <algorithm>
 
 #include "fva_internal.hpp"
@@ -477,30 +477,16 @@ __global__ __launch_bounds__(kPlanThreads) void xcd_assign_kernel(const int32_t*
     base[h] = ws[AttnWs::kXcdOff + hx[h]] + hpos[h] * nB;
 }
 
-// XCD plan, step 2 (one workgroup per head): the head's rows heaviest first
-// (row count descending, ties by query block ascending) at its base.
-__global__ __launch_bounds__(kPlanThreads) void xcd_fill_kernel(const int32_t* row_count, int nB,
-                                                                int32_t* ws, int64_t nheads) {
-  __shared__ uint32_t keys[2048];
+// XCD plan, step 2 (one workgroup per head): the head's rows in query-block
+// order at its base.  Neighbouring query blocks select mostly the same key
+// blocks, so the workgroups resident on one XCD stream shared K/V tiles
+// through that XCD's L2; balance comes from the head placement and stealing.
+__global__ __launch_bounds__(kPlanThreads) void xcd_fill_kernel(int nB, int32_t* ws,
+                                                                int64_t nheads) {
   const int64_t h = blockIdx.x;
-  int P = 1;
-  while (P < nB) P <<= 1;
-  for (int i = threadIdx.x; i < P; i += kPlanThreads)
-    keys[i] = i < nB ? ((uint32_t)(nB - row_count[h * nB + i]) << 11) | (uint32_t)i : ~0u;
-  __syncthreads();
-  for (int k = 2; k <= P; k <<= 1)
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int q = threadIdx.x; q < P / 2; q += kPlanThreads) {
-        const int i = 2 * j * (q / j) + (q % j), l = i + j;
-        const uint32_t x = keys[i], y = keys[l];
-        if ((x > y) == ((i & k) == 0)) { keys[i] = y; keys[l] = x; }
-      }
-      __syncthreads();
-    }
   const int32_t base = ws[AttnWs::head_base_off() / 4 + h];
   int32_t* xq = ws + AttnWs::xq_off(nheads) / 4;
-  for (int i = threadIdx.x; i < nB; i += kPlanThreads)
-    xq[base + i] = (int32_t)(h * nB + (keys[i] & 2047u));
+  for (int i = threadIdx.x; i < nB; i += kPlanThreads) xq[base + i] = (int32_t)(h * nB + i);
 }
 
 constexpr int kQT = 1;  // 32-query tiles per wave in the launched kernels
@@ -535,8 +521,8 @@ fva_status launch_t(const Problem& p, AttnArgs a, int flags, bool dense, hipStre
     const int nheads = p.B * p.Hh;
     hipLaunchKernelGGL(xcd_assign_kernel, dim3(1), dim3(kPlanThreads), 0, s, a.head_count, nheads,
                        p.nB, a.ws);
-    hipLaunchKernelGGL(xcd_fill_kernel, dim3(nheads), dim3(kPlanThreads), 0, s, a.row_count, p.nB,
-                       a.ws, (int64_t)nheads);
+    hipLaunchKernelGGL(xcd_fill_kernel, dim3(nheads), dim3(kPlanThreads), 0, s, p.nB, a.ws,
+                       (int64_t)nheads);
     a.queue = a.ws + AttnWs::xq_off(nheads) / 4;
     if (trace) FVA_LAUNCH(FVA_SCHED_XCD, true, persist);
     else FVA_LAUNCH(FVA_SCHED_XCD, false, persist);

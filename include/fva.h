@@ -115,11 +115,11 @@ typedef struct {
                                  rows in row order (fixed placement)         */
 #define FVA_SCHED_GRID   0x2  /* one workgroup per queue entry, hardware
                                  dispatch                                    */
-#define FVA_SCHED_XCD    0x3  /* persistent, XCD-aware: heads assigned to the
-                                 8 XCDs by longest-processing-time on W_h;
-                                 each XCD pops its heads' rows heaviest first
-                                 and steals from the others when it runs dry
-                                 (at most 4096 heads)                        */
+#define FVA_SCHED_XCD    0x3  /* persistent, XCD-aware: heads placed on the
+                                 8 XCDs heaviest first (longest-processing-
+                                 time on W_h); each XCD pops its heads' rows
+                                 in query-block order and steals from the
+                                 others when it runs dry (at most 4096 heads) */
 #define FVA_TRACE        0x10 /* write one trace record per item             */
 
 /* fva_reorder directions and layouts */
