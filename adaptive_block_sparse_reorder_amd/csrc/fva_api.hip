@@ -67,6 +67,12 @@ RouteWs route_ws_layout(const Problem& p) {
   off = align256(off + (size_t)p.rows * p.d * sizeof(float));
   L.thresh_off = off;
   off = align256(off + (size_t)p.B * p.Hh * sizeof(uint64_t));
+  L.qtmp_row_off = off;
+  off = align256(off + (size_t)p.rows * sizeof(int32_t));
+  L.qtmp_rank_off = off;
+  off = align256(off + (size_t)p.rows * sizeof(int32_t));
+  L.qhist_off = off;
+  off = align256(off + (size_t)((p.rows + 1023) / 1024) * (p.nB + 1) * sizeof(int32_t));
   L.total = off;
   return L;
 }

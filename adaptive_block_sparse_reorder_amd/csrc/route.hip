@@ -413,71 +413,102 @@ __global__ __launch_bounds__(kRouteThreads) void topup_apply_kernel(
 }
 
 // ------------------------------------------------------------------ queue
-// One 1024-thread workgroup: stable counting sort of rows by count,
-// descending.  Rounds of 1024 rows are sorted in LDS by (count desc, row);
-// each row lands at the running offset of its count plus its rank in the run.
+// Stable counting sort of rows by count, descending, in three launches:
+//   1. per chunk of 1024 rows: sort (count desc, row) in LDS, record each
+//      row's rank inside its run of equal counts, and the chunk's run lengths;
+//   2. one exclusive scan over (count descending, chunk ascending) turns the
+//      run lengths into output offsets;
+//   3. scatter: queue[offset(chunk, count) + rank] = row.
 constexpr int kQThreads = 1024;
 
-__global__ __launch_bounds__(kQThreads) void queue_kernel(const int32_t* __restrict__ row_count,
-                                                          int64_t rows, int nB,
-                                                          int32_t* __restrict__ queue) {
-  __shared__ int32_t off[kMaxNB + 2];
+__global__ __launch_bounds__(kQThreads) void queue_chunk_kernel(
+    const int32_t* __restrict__ row_count, int64_t rows, int nB, int32_t* __restrict__ tmp_row,
+    int32_t* __restrict__ tmp_rank, int32_t* __restrict__ hist) {
   __shared__ uint32_t keys[kQThreads];
-  __shared__ int32_t start[kQThreads];
+  __shared__ int32_t lhist[kMaxNB + 1];
   __shared__ int32_t wtot[kQThreads / 64];
-  const int nbins = nB + 1;
-  for (int c = threadIdx.x; c < nbins; c += kQThreads) off[c] = 0;
+  const int64_t base = (int64_t)blockIdx.x * kQThreads;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  for (int c = threadIdx.x; c <= nB; c += kQThreads) lhist[c] = 0;
+  const int64_t item = base + threadIdx.x;
+  keys[threadIdx.x] = item < rows
+                          ? ((uint32_t)(nB - row_count[item]) << 10) | (uint32_t)threadIdx.x
+                          : 0xffffffffu;
   __syncthreads();
-  for (int64_t r = threadIdx.x; r < rows; r += kQThreads) atomicAdd(&off[row_count[r]], 1);
+  bitonic_sort<uint32_t, kQThreads>(keys, kQThreads);
+  const uint32_t k = keys[threadIdx.x];
+  const bool valid = k != 0xffffffffu;
+  const uint32_t grp = k >> 10;
+  const bool head = threadIdx.x == 0 || (keys[threadIdx.x - 1] >> 10) != grp;
+  int st = head ? (int)threadIdx.x : 0;  // inclusive max-scan of run starts
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(st, o, 64);
+    if (lane >= o) st = max(st, v);
+  }
+  if (lane == 63) wtot[wave] = st;
   __syncthreads();
-  // exclusive scan in descending count order, sequential per wave chunk
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int c = nB; c >= 0; --c) {
-      const int h = off[c];
-      off[c] = run;
-      run += h;
-    }
+  int carry = 0;
+  for (int w = 0; w < wave; ++w) carry = max(carry, wtot[w]);
+  st = max(st, carry);
+  if (valid) {
+    tmp_row[base + threadIdx.x] = (int32_t)(base + (k & 1023u));
+    tmp_rank[base + threadIdx.x] = (int)threadIdx.x - st;
+    const bool tail = threadIdx.x == kQThreads - 1 || (keys[threadIdx.x + 1] >> 10) != grp;
+    if (tail) lhist[nB - (int)grp] = (int)threadIdx.x - st + 1;
   }
   __syncthreads();
+  int32_t* h = hist + (int64_t)blockIdx.x * (nB + 1);
+  for (int c = threadIdx.x; c <= nB; c += kQThreads) h[c] = lhist[c];
+}
+
+// In-place exclusive scan of hist[chunk][c] in the order (c descending,
+// chunk ascending): one workgroup, tiles of 1024 with a running carry.
+__global__ __launch_bounds__(kQThreads) void queue_scan_kernel(int32_t* __restrict__ hist,
+                                                               int64_t nchunks, int nB) {
+  __shared__ int32_t wtot[kQThreads / 64];
+  __shared__ int32_t s_carry;
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-  for (int64_t base = 0; base < rows; base += kQThreads) {
-    const int64_t item = base + threadIdx.x;
-    keys[threadIdx.x] = item < rows
-                            ? ((uint32_t)(nB - row_count[item]) << 10) | (uint32_t)threadIdx.x
-                            : 0xffffffffu;
-    __syncthreads();
-    bitonic_sort<uint32_t, kQThreads>(keys, kQThreads);
-    const uint32_t k = keys[threadIdx.x];
-    const bool valid = k != 0xffffffffu;
-    const uint32_t grp = k >> 10;
-    const bool head = threadIdx.x == 0 || (keys[threadIdx.x - 1] >> 10) != grp;
-    // inclusive max-scan of run starts
-    int st = head ? (int)threadIdx.x : 0;
+  const int64_t E = (int64_t)(nB + 1) * nchunks;
+  if (threadIdx.x == 0) s_carry = 0;
+  __syncthreads();
+  for (int64_t e0 = 0; e0 < E; e0 += kQThreads) {
+    const int64_t e = e0 + threadIdx.x;
+    int64_t idx = -1;
+    int v = 0;
+    if (e < E) {
+      const int c = nB - (int)(e / nchunks);
+      const int64_t ch = e % nchunks;
+      idx = ch * (nB + 1) + c;
+      v = hist[idx];
+    }
+    int x = v;  // inclusive wave scan
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(st, o, 64);
-      if (lane >= o) st = max(st, v);
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
     }
-    if (lane == 63) wtot[wave] = st;
+    if (lane == 63) wtot[wave] = x;
     __syncthreads();
-    int carry = 0;
-    for (int w = 0; w < wave; ++w) carry = max(carry, wtot[w]);
-    st = max(st, carry);
-    start[threadIdx.x] = st;
+    int before = s_carry;
+    for (int w = 0; w < wave; ++w) before += wtot[w];
+    if (idx >= 0) hist[idx] = before + x - v;
     __syncthreads();
-    if (valid) {
-      const int c = nB - (int)grp;
-      const int rank = (int)threadIdx.x - st;
-      queue[off[c] + rank] = (int32_t)(base + (k & 1023u));
-    }
-    __syncthreads();
-    if (valid) {
-      const bool tail = threadIdx.x == kQThreads - 1 || (keys[threadIdx.x + 1] >> 10) != grp;
-      if (tail) off[nB - (int)grp] += (int)threadIdx.x - st + 1;
-    }
+    if (threadIdx.x == kQThreads - 1) s_carry = before + x;
     __syncthreads();
   }
+}
+
+__global__ void queue_scatter_kernel(const int32_t* __restrict__ tmp_row,
+                                     const int32_t* __restrict__ tmp_rank,
+                                     const int32_t* __restrict__ hist,
+                                     const int32_t* __restrict__ row_count, int64_t rows, int nB,
+                                     int32_t* __restrict__ queue) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rows) return;
+  const int32_t row = tmp_row[t];
+  const int64_t chunk = t / kQThreads;
+  queue[hist[chunk * (nB + 1) + row_count[row]] + tmp_rank[t]] = row;
 }
 
 }  // namespace
@@ -521,8 +552,15 @@ fva_status launch_route(const Problem& p, const void* qr, const void* kr,
                        m.scores, p.nB, p.words, thresh, m.bitmask, m.row_count, m.col_idx,
                        m.head_count);
   }
-  hipLaunchKernelGGL(queue_kernel, dim3(1), dim3(kQThreads), 0, s, m.row_count, p.rows, p.nB,
-                     m.queue);
+  const int64_t nchunks = (p.rows + kQThreads - 1) / kQThreads;
+  int32_t* tmp_row = (int32_t*)(ws + L.qtmp_row_off);
+  int32_t* tmp_rank = (int32_t*)(ws + L.qtmp_rank_off);
+  int32_t* hist = (int32_t*)(ws + L.qhist_off);
+  hipLaunchKernelGGL(queue_chunk_kernel, dim3((unsigned)nchunks), dim3(kQThreads), 0, s,
+                     m.row_count, p.rows, p.nB, tmp_row, tmp_rank, hist);
+  hipLaunchKernelGGL(queue_scan_kernel, dim3(1), dim3(kQThreads), 0, s, hist, nchunks, p.nB);
+  hipLaunchKernelGGL(queue_scatter_kernel, dim3((unsigned)((p.rows + 255) / 256)), dim3(256), 0,
+                     s, tmp_row, tmp_rank, hist, m.row_count, p.rows, p.nB, m.queue);
   return hip_fail(hipGetLastError(), "route launch");
 }
 
