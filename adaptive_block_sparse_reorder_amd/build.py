@@ -31,7 +31,7 @@ CFLAGS = [
     "-Wall", "-Wno-unused-result",
 ]
 
-SOURCES = ["fva_api.hip", "reorder.hip", "route.hip", "attn.hip"]
+SOURCES = ["fva_api.hip", "reorder.hip", "route.hip", "attn.hip", "rlb_host.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -175,6 +175,23 @@ fva_status fva_route(const void* qr, const void* kr, int32_t B, int32_t Hh, int3
   return launch_route(p, qr, kr, *params, scale, *mask, (char*)ws, flags, stream);
 }
 
+fva_status fva_topup(int32_t B, int32_t Hh, int32_t d, const fva_grid* grid,
+                     const int64_t* head_budget, const fva_mask* mask, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  Problem p;
+  fva_status st = make_problem(grid, B, Hh, d, &p);
+  if (st != FVA_OK) return st;
+  if (!head_budget) return fail(FVA_ERR_INVALID_ARG, "head_budget is null");
+  st = check_mask(mask, true);
+  if (st != FVA_OK) return st;
+  const size_t need = route_ws_layout(p).total;
+  if (!ws || ws_bytes < need)
+    return fail(FVA_ERR_WORKSPACE, "route workspace needs %zu bytes, got %zu", need,
+                ws ? ws_bytes : (size_t)0);
+  if (((uintptr_t)ws & 255u) != 0) return fail(FVA_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  return launch_topup(p, head_budget, *mask, (char*)ws, stream);
+}
+
 fva_status fva_route_flags(const void* ws, uint32_t* flags_out, hipStream_t stream) {
   if (!ws || !flags_out) return fail(FVA_ERR_INVALID_ARG, "null pointer");
   hipError_t e = hipMemcpyAsync(flags_out, ws, sizeof(uint32_t), hipMemcpyDeviceToHost, stream);

@@ -51,6 +51,8 @@ fva_status launch_reorder(const Problem& p, const void* src, void* dst, const in
 fva_status launch_route(const Problem& p, const void* qr, const void* kr,
                         const fva_route_params& prm, float scale, const fva_mask& m,
                         char* ws, int flags, hipStream_t s);
+fva_status launch_topup(const Problem& p, const int64_t* budgets, const fva_mask& m, char* ws,
+                        hipStream_t s);
 fva_status launch_attn(const Problem& p, const void* qr, const void* kr, const void* vt,
                        void* out, const fva_mask* m, float scale, int flags, void* ws,
                        void* trace, bool dense, hipStream_t s);

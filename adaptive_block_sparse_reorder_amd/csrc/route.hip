@@ -320,19 +320,20 @@ __device__ __forceinline__ uint64_t pair_key(float s, int i, int j) {
 constexpr int kSelThreads = 1024;
 
 // One workgroup per head: exact radix select (8-bit digits, 8 passes) of the
-// need-th smallest priority key among unselected pairs.  thresh[bh] is an
+// need-th smallest priority key among unselected pairs, need = budget - W_h
+// with the budget per head (budgets[bh]) or shared (budget).  thresh[bh] is an
 // exclusive bound: pairs with key < thresh are added; 0 means none.
 __global__ __launch_bounds__(kSelThreads) void topup_select_kernel(
     const float* __restrict__ S, const uint32_t* __restrict__ bitmask,
     const int32_t* __restrict__ head_count, int nB, int words, int64_t budget,
-    uint64_t* __restrict__ thresh) {
+    const int64_t* __restrict__ budgets, uint64_t* __restrict__ thresh) {
   __shared__ uint32_t hist[256];
   __shared__ uint64_t s_prefix;
   __shared__ int64_t s_need;
   const int64_t bh = blockIdx.x;
   const int64_t pairs = (int64_t)nB * nB;
   const int64_t W = head_count[bh];
-  int64_t need = budget - W;
+  int64_t need = (budgets ? budgets[bh] : budget) - W;
   if (need <= 0) {
     if (threadIdx.x == 0) thresh[bh] = 0ull;
     return;
@@ -513,6 +514,35 @@ __global__ void queue_scatter_kernel(const int32_t* __restrict__ tmp_row,
 
 }  // namespace
 
+namespace {
+
+void launch_topup_kernels(const Problem& p, const fva_mask& m, char* ws, int64_t budget,
+                          const int64_t* budgets, hipStream_t s) {
+  const RouteWs L = route_ws_layout(p);
+  uint64_t* thresh = (uint64_t*)(ws + L.thresh_off);
+  const int nheads = p.B * p.Hh;
+  hipLaunchKernelGGL(topup_select_kernel, dim3(nheads), dim3(kSelThreads), 0, s, m.scores,
+                     m.bitmask, m.head_count, p.nB, p.words, budget, budgets, thresh);
+  hipLaunchKernelGGL(topup_apply_kernel, dim3((unsigned)p.rows), dim3(kRouteThreads), 0, s,
+                     m.scores, p.nB, p.words, thresh, m.bitmask, m.row_count, m.col_idx,
+                     m.head_count);
+}
+
+void launch_queue(const Problem& p, const fva_mask& m, char* ws, hipStream_t s) {
+  const RouteWs L = route_ws_layout(p);
+  const int64_t nchunks = (p.rows + kQThreads - 1) / kQThreads;
+  int32_t* tmp_row = (int32_t*)(ws + L.qtmp_row_off);
+  int32_t* tmp_rank = (int32_t*)(ws + L.qtmp_rank_off);
+  int32_t* hist = (int32_t*)(ws + L.qhist_off);
+  hipLaunchKernelGGL(queue_chunk_kernel, dim3((unsigned)nchunks), dim3(kQThreads), 0, s,
+                     m.row_count, p.rows, p.nB, tmp_row, tmp_rank, hist);
+  hipLaunchKernelGGL(queue_scan_kernel, dim3(1), dim3(kQThreads), 0, s, hist, nchunks, p.nB);
+  hipLaunchKernelGGL(queue_scatter_kernel, dim3((unsigned)((p.rows + 255) / 256)), dim3(256), 0,
+                     s, tmp_row, tmp_rank, hist, m.row_count, p.rows, p.nB, m.queue);
+}
+
+}  // namespace
+
 fva_status launch_route(const Problem& p, const void* qr, const void* kr,
                         const fva_route_params& prm, float scale, const fva_mask& m,
                         char* ws, int flags, hipStream_t s) {
@@ -520,7 +550,6 @@ fva_status launch_route(const Problem& p, const void* qr, const void* kr,
   uint32_t* wflags = (uint32_t*)(ws + L.flags_off);
   float* qbar = (float*)(ws + L.qbar_off);
   float* kbar = (float*)(ws + L.kbar_off);
-  uint64_t* thresh = (uint64_t*)(ws + L.thresh_off);
   const int nheads = p.B * p.Hh;
   hipLaunchKernelGGL(zero_route_state, dim3((nheads + 255) / 256), dim3(256), 0, s,
                      m.head_count, nheads, wflags);
@@ -545,23 +574,16 @@ fva_status launch_route(const Problem& p, const void* qr, const void* kr,
   hipLaunchKernelGGL(route_kernel, dim3((unsigned)p.rows), dim3(kRouteThreads), 0, s, m.scores,
                      p.nB, p.words, P, prm.top_p, prm.topk_floor, m.bitmask, m.row_count,
                      m.col_idx, m.head_count, wflags);
-  if (prm.aug_budget > 0) {
-    hipLaunchKernelGGL(topup_select_kernel, dim3(nheads), dim3(kSelThreads), 0, s, m.scores,
-                       m.bitmask, m.head_count, p.nB, p.words, (int64_t)prm.aug_budget, thresh);
-    hipLaunchKernelGGL(topup_apply_kernel, dim3((unsigned)p.rows), dim3(kRouteThreads), 0, s,
-                       m.scores, p.nB, p.words, thresh, m.bitmask, m.row_count, m.col_idx,
-                       m.head_count);
-  }
-  const int64_t nchunks = (p.rows + kQThreads - 1) / kQThreads;
-  int32_t* tmp_row = (int32_t*)(ws + L.qtmp_row_off);
-  int32_t* tmp_rank = (int32_t*)(ws + L.qtmp_rank_off);
-  int32_t* hist = (int32_t*)(ws + L.qhist_off);
-  hipLaunchKernelGGL(queue_chunk_kernel, dim3((unsigned)nchunks), dim3(kQThreads), 0, s,
-                     m.row_count, p.rows, p.nB, tmp_row, tmp_rank, hist);
-  hipLaunchKernelGGL(queue_scan_kernel, dim3(1), dim3(kQThreads), 0, s, hist, nchunks, p.nB);
-  hipLaunchKernelGGL(queue_scatter_kernel, dim3((unsigned)((p.rows + 255) / 256)), dim3(256), 0,
-                     s, tmp_row, tmp_rank, hist, m.row_count, p.rows, p.nB, m.queue);
+  if (prm.aug_budget > 0) launch_topup_kernels(p, m, ws, (int64_t)prm.aug_budget, nullptr, s);
+  launch_queue(p, m, ws, s);
   return hip_fail(hipGetLastError(), "route launch");
+}
+
+fva_status launch_topup(const Problem& p, const int64_t* budgets, const fva_mask& m, char* ws,
+                        hipStream_t s) {
+  launch_topup_kernels(p, m, ws, 0, budgets, s);
+  launch_queue(p, m, ws, s);
+  return hip_fail(hipGetLastError(), "top-up launch");
 }
 
 }  // namespace fva

@@ -36,6 +36,9 @@ FVA_INVERSE = 1
 FVA_LAYOUT_ROWS = 0
 FVA_LAYOUT_V64 = 1
 FVA_LAYOUT_K64 = 2
+FVA_RLB_PAIRS = 0
+FVA_RLB_RING = 1
+FVA_RLB_MAX_PAIR_RANKS = 12
 
 
 class fva_grid(ctypes.Structure):
@@ -59,6 +62,13 @@ class fva_mask(ctypes.Structure):
     _fields_ = [("scores", ctypes.c_void_p), ("bitmask", ctypes.c_void_p),
                 ("row_count", ctypes.c_void_p), ("col_idx", ctypes.c_void_p),
                 ("head_count", ctypes.c_void_p), ("queue", ctypes.c_void_p)]
+
+
+class fva_rlb_stats(ctypes.Structure):
+    _fields_ = [("max_before", ctypes.c_int64), ("max_after", ctypes.c_int64),
+                ("mean", ctypes.c_double), ("lambda_before", ctypes.c_double),
+                ("lambda_after", ctypes.c_double), ("solve_us", ctypes.c_double),
+                ("migrations", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class FvaError(RuntimeError):
@@ -91,8 +101,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fva_sparse_attn.argtypes = [P, P, P, P, I32, I32, I32, ctypes.POINTER(fva_grid),
                                     ctypes.POINTER(fva_mask), F, I32, P, SZ, P, P]
     lib.fva_dense_attn.argtypes = [P, P, P, P, I32, I32, I32, ctypes.POINTER(fva_grid), F, P]
+    PI32 = ctypes.POINTER(ctypes.c_int32)
+    PI64 = ctypes.POINTER(ctypes.c_int64)
+    lib.fva_rlb_plan.argtypes = [PI32, I32, I32, I32, PI32, PI32, PI32,
+                                 ctypes.POINTER(fva_rlb_stats)]
+    lib.fva_sasa_budget.argtypes = [PI32, I32, I32, PI32, F, I64, PI64, PI64]
+    lib.fva_topup.argtypes = [I32, I32, I32, ctypes.POINTER(fva_grid), P,
+                              ctypes.POINTER(fva_mask), P, SZ, P]
     for fn in ("fva_sizes", "fva_reorder", "fva_route", "fva_route_flags", "fva_sparse_attn",
-               "fva_dense_attn"):
+               "fva_dense_attn", "fva_rlb_plan", "fva_sasa_budget", "fva_topup"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.fva_status_string.argtypes = [ctypes.c_int]
     lib.fva_status_string.restype = ctypes.c_char_p
@@ -178,6 +195,44 @@ def fva_dense_attn(qr, kr, vt, out, B: int, Hh: int, d: int, grid: fva_grid, sca
     lib = load_library()
     _check(lib.fva_dense_attn(_ptr(qr), _ptr(kr), _ptr(vt), _ptr(out), B, Hh, d,
                               ctypes.byref(grid), scale, _stream(stream)), "fva_dense_attn")
+
+
+def fva_rlb_plan(head_count, ranks: int, topology: int = FVA_RLB_PAIRS):
+    """Host planner.  head_count: sequence of per-head workloads W_h.
+    Returns (send_to, send_head, rank_of_head, stats)."""
+    lib = load_library()
+    W = [int(x) for x in head_count]
+    n = len(W)
+    hc = (ctypes.c_int32 * n)(*W)
+    to = (ctypes.c_int32 * ranks)()
+    hd = (ctypes.c_int32 * ranks)()
+    roh = (ctypes.c_int32 * n)()
+    st = fva_rlb_stats()
+    _check(lib.fva_rlb_plan(hc, n, ranks, topology, to, hd, roh, ctypes.byref(st)),
+           "fva_rlb_plan")
+    return list(to), list(hd), list(roh), st
+
+
+def fva_sasa_budget(head_count, ranks: int, rank_of_head, alpha: float, head_cap: int):
+    """Host budgets.  Returns (head_budget, rank_load_after) as lists."""
+    lib = load_library()
+    W = [int(x) for x in head_count]
+    n = len(W)
+    hc = (ctypes.c_int32 * n)(*W)
+    roh = (ctypes.c_int32 * n)(*[int(x) for x in rank_of_head])
+    hb = (ctypes.c_int64 * n)()
+    rl = (ctypes.c_int64 * ranks)()
+    _check(lib.fva_sasa_budget(hc, n, ranks, roh, float(alpha), int(head_cap), hb, rl),
+           "fva_sasa_budget")
+    return list(hb), list(rl)
+
+
+def fva_topup(B: int, Hh: int, d: int, grid: fva_grid, head_budget, mask: fva_mask, ws,
+              ws_bytes: int, stream=None):
+    """Device top-up with per-head budgets (head_budget: device int64 [B*Hh])."""
+    lib = load_library()
+    _check(lib.fva_topup(B, Hh, d, ctypes.byref(grid), _ptr(head_budget), ctypes.byref(mask),
+                         _ptr(ws), ws_bytes, _stream(stream)), "fva_topup")
 
 
 # --------------------------------------------------------------------------

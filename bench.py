@@ -247,6 +247,32 @@ def main():
             lam[name] = lambda_cu(buf.trace.cpu().numpy().view(np.uint32), int(buf.sizes.rows))
         extras["lambda_cu"] = lam
 
+    # runtime load balancing on 8 virtual ranks from the realized workloads
+    hc = buf.head_count.cpu().numpy().astype(np.int64).tolist()
+    rlb = {}
+    for name, topo in (("pairs", F.FVA_RLB_PAIRS), ("ring", F.FVA_RLB_RING)):
+        _, _, roh, st = F.fva_rlb_plan(hc, 8, topo)
+        rlb[name] = {"lambda_before": round(st.lambda_before, 4),
+                     "lambda_after": round(st.lambda_after, 4),
+                     "migrations": int(st.migrations), "solve_us": round(st.solve_us, 1)}
+        if name == "pairs":
+            roh_pairs = roh
+    extras["rlb_8_virtual_ranks"] = rlb
+    # slack-aware augmentation after balancing (alpha 0.5), applied on the device
+    budgets, rank_after = F.fva_sasa_budget(hc, 8, roh_pairs, 0.5, w.nB * w.nB)
+    dev_budgets = torch.tensor(budgets, dtype=torch.int64, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    F.fva_topup(w.B, w.Hh, w.d, g, dev_budgets, m, buf.route_ws, buf.sizes.route_ws_bytes)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    extras["sasa_alpha_0.5"] = {
+        "topup_ms": round(e0.elapsed_time(e1), 4),
+        "pairs_added": int(sum(budgets) - sum(hc)),
+        "rank_max_after": int(max(rank_after)),
+        "density_after": round(float(buf.head_count.sum().item()) / (w.Hh * w.B * w.nB ** 2), 4),
+    }
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu oracle baseline")

@@ -202,6 +202,62 @@ fva_status fva_dense_attn(const void* qr, const void* kr, const void* vt, void* 
                           int32_t B, int32_t Hh, int32_t d, const fva_grid* grid,
                           float scale, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Load balancing and slack-aware augmentation on virtual ranks (FVAttn
+ * sections 3.2 and 3.3).  Host functions: all pointers are HOST pointers.
+ * ---------------------------------------------------------------------- */
+#define FVA_RLB_PAIRS 0           /* plans are disjoint rank swaps (involutions)  */
+#define FVA_RLB_RING 1            /* every rank sends one head to rank r+1 mod R */
+#define FVA_RLB_MAX_PAIR_RANKS 12 /* the pair search enumerates every matching   */
+
+typedef struct {
+  int64_t max_before;        /* critical-path rank load before balancing      */
+  int64_t max_after;         /* ... after                                     */
+  double mean;               /* mean rank load                                */
+  double lambda_before;      /* load-imbalance factor max/mean before         */
+  double lambda_after;       /* ... after                                     */
+  double solve_us;           /* planner wall time                             */
+  int32_t migrations;        /* ranks that send a head                        */
+  int32_t reserved;
+} fva_rlb_stats;
+
+/* Runtime load balancing (section 3.2) on R virtual ranks.  head_count[h] is
+ * the realized workload W_h (selected block pairs, as fva_route writes it).
+ * Heads start on ranks by contiguous Ulysses placement: head h on rank
+ * floor(h*R/nheads).  A plan is a permutation of the ranks in which rank r
+ * sends one local head to send_to[r] and receives one; fixed points send
+ * nothing (send_to[r] = send_head[r] = -1).  The plan minimizes the largest
+ * rank load first and the sum of squared rank loads second (equivalently the
+ * variance), exactly over the chosen topology; when no plan shortens the
+ * critical path, no head moves.  Outputs: send_to[ranks], send_head[ranks]
+ * (global head ids), rank_of_head[nheads] after migration, stats.
+ * FVA_RLB_PAIRS needs ranks <= FVA_RLB_MAX_PAIR_RANKS.                      */
+fva_status fva_rlb_plan(const int32_t* head_count, int32_t nheads, int32_t ranks,
+                        int32_t topology, int32_t* send_to, int32_t* send_head,
+                        int32_t* rank_of_head, fva_rlb_stats* stats);
+
+/* Slack-aware augmentation budgets (section 3.3).  With rank loads L_r from
+ * rank_of_head, rank r's slack is max_r L_r - L_r and its extra budget is
+ * floor(alpha * slack) pairs (alpha = augmentation coefficient in [0, 1]),
+ * split evenly over the rank's heads in ascending head id (remainder to the
+ * lowest ids).  head_budget[h] = W_h + extra share, capped at
+ * max(head_cap, W_h) (head_cap = nB*nB: all pairs).  rank_load_after
+ * (nullable, [ranks]) receives the budgeted rank loads.  Pass head_budget to
+ * fva_topup on the device.                                                  */
+fva_status fva_sasa_budget(const int32_t* head_count, int32_t nheads, int32_t ranks,
+                           const int32_t* rank_of_head, float alpha, int64_t head_cap,
+                           int64_t* head_budget, int64_t* rank_load_after);
+
+/* Per-head top-up of an existing mask (section 3.3, device): every head whose
+ * W_h (mask->head_count) is below head_budget[h] (DEVICE int64 [B*Hh]) gains
+ * the head_budget[h] - W_h unselected pairs of highest score in mask->scores
+ * (ties: query block ascending, then key block ascending); bitmask, row
+ * counts, column lists, head_count and the heaviest-first queue are then
+ * rewritten.  ws is a route workspace (fva_sizes().route_ws_bytes).         */
+fva_status fva_topup(int32_t B, int32_t Hh, int32_t d, const fva_grid* grid,
+                     const int64_t* head_budget, const fva_mask* mask, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
+
 /* Human-readable status name, and the calling thread's last error detail. */
 const char* fva_status_string(fva_status s);
 const char* fva_last_error(void);

@@ -23,6 +23,10 @@ Steps and the passages they follow (all on the FVAttn page):
   sasa_topup                         section 3.3 (extra budget spent in the
                                      importance order produced by routing), one-GPU
                                      per-head form
+  rlb_plan / sasa_budget             section 3.2 (one-send-one-receive head
+                                     migration, lexicographic objective) and
+                                     section 3.3 (slack times the augmentation
+                                     coefficient), on virtual ranks
   heaviest_first                     section 3.2 (load balancing on realized
                                      workloads), one-GPU work-queue form
   sparse_attention                   section 2 (only selected query-key block pairs
@@ -34,6 +38,7 @@ tiny inputs, or a library routine for a special case (dense attention).
 
 from __future__ import annotations
 
+import itertools
 import math
 from typing import Dict, Iterable, List, Optional, Sequence, Tuple
 
@@ -190,20 +195,23 @@ def head_workload(mask: np.ndarray) -> np.ndarray:
     return mask.reshape(mask.shape[0], mask.shape[1], -1).sum(axis=-1).astype(np.int64)
 
 
-def sasa_topup(S32: np.ndarray, mask: np.ndarray, budget: int) -> np.ndarray:
+def sasa_topup(S32: np.ndarray, mask: np.ndarray, budget) -> np.ndarray:
     """One-GPU form of slack-aware augmentation: per head, when its workload
-    W_h is below `budget` pairs, add the budget - W_h unselected pairs with the
-    highest scores (ties: query block ascending, then key block ascending).
-    Heads at or above the budget are unchanged.  budget <= 0 disables it."""
+    W_h is below its budget (pairs), add the budget - W_h unselected pairs with
+    the highest scores (ties: query block ascending, then key block ascending).
+    Heads at or above the budget are unchanged.  `budget` is one number for
+    every head (<= 0 disables it) or an array with one budget per (b, h)."""
     out = mask.copy()
-    if budget <= 0:
-        return out
     B, Hh, nB, _ = mask.shape
+    per_head = np.ndim(budget) > 0
+    if not per_head and budget <= 0:
+        return out
     ii, jj = np.meshgrid(np.arange(nB), np.arange(nB), indexing="ij")
     for b in range(B):
         for h in range(Hh):
             m = out[b, h]
-            need = budget - int(m.sum())
+            bud = int(np.asarray(budget).reshape(-1)[b * Hh + h]) if per_head else int(budget)
+            need = bud - int(m.sum())
             if need <= 0:
                 continue
             free = ~m
@@ -220,6 +228,119 @@ def heaviest_first(counts: np.ndarray) -> np.ndarray:
     flat = counts.reshape(-1)
     ids = np.arange(flat.shape[0])
     return np.array(sorted(ids.tolist(), key=lambda t: (-int(flat[t]), t)), dtype=np.int64)
+
+
+# --------------------------------------------------------------------------
+# Runtime load balancing on virtual ranks (section 3.2) and slack-aware
+# budgets (section 3.3)
+# --------------------------------------------------------------------------
+
+def contiguous_placement(nheads: int, ranks: int) -> np.ndarray:
+    """Ulysses head placement: head h on rank floor(h * R / nheads)."""
+    return np.array([h * ranks // nheads for h in range(nheads)], dtype=np.int64)
+
+
+def rank_loads(W, rank_of_head, ranks: int) -> np.ndarray:
+    """L_r = sum of W_h over the heads on rank r."""
+    L = np.zeros(ranks, dtype=np.int64)
+    for h, r in enumerate(rank_of_head):
+        L[r] += int(W[h])
+    return L
+
+
+def plan_objective(loads) -> Tuple[int, int]:
+    """Lexicographic objective of a plan: (critical-path load max_r L_r,
+    sum of squared loads).  With the total fixed, the second term orders plans
+    by rank-load variance."""
+    loads = [int(x) for x in loads]
+    return max(loads), sum(x * x for x in loads)
+
+
+def _involutions(n: int):
+    """All involutions of range(n) as mate lists (mate[r] = r for fixed points)."""
+    def rec(mate, r):
+        while r < n and mate[r] is not None:
+            r += 1
+        if r == n:
+            yield list(mate)
+            return
+        mate[r] = r
+        yield from rec(mate, r + 1)
+        for s in range(r + 1, n):
+            if mate[s] is None:
+                mate[r], mate[s] = s, r
+                yield from rec(mate, r + 1)
+                mate[s] = None
+        mate[r] = None
+    yield from rec([None] * n, 0)
+
+
+def rlb_plans(W, ranks: int, topology: str):
+    """Every plan of the topology: (send_to, send_head) per rank, -1 = none.
+    A plan is a permutation pi of the ranks; rank r sends one of its heads to
+    pi(r).  'pairs': pi an involution (swaps); 'ring': pi(r) = r + 1 mod R with
+    every rank sending.  The identity plan is always included."""
+    nheads = len(W)
+    place = contiguous_placement(nheads, ranks)
+    heads = [[h for h in range(nheads) if place[h] == r] for r in range(ranks)]
+    yield [-1] * ranks, [-1] * ranks
+    if topology == "pairs":
+        perms = [m for m in _involutions(ranks) if any(m[r] != r for r in range(ranks))]
+    elif topology == "ring":
+        perms = [[(r + 1) % ranks for r in range(ranks)]] if ranks >= 2 else []
+    else:
+        raise ValueError(topology)
+    for pi in perms:
+        movers = [r for r in range(ranks) if pi[r] != r]
+        for choice in itertools.product(*[heads[r] for r in movers]):
+            to, hd = [-1] * ranks, [-1] * ranks
+            for r, a in zip(movers, choice):
+                to[r], hd[r] = pi[r], a
+            yield to, hd
+
+
+def apply_plan(nheads: int, ranks: int, send_to, send_head) -> np.ndarray:
+    place = contiguous_placement(nheads, ranks)
+    for r in range(ranks):
+        if send_to[r] >= 0:
+            place[send_head[r]] = send_to[r]
+    return place
+
+
+def rlb_plan(W, ranks: int, topology: str):
+    """Brute force over every plan of the topology; the best objective, and
+    one plan reaching it.  When no plan lowers the critical path the identity
+    is returned (migrating without benefit only costs communication)."""
+    nheads = len(W)
+    ident = plan_objective(rank_loads(W, contiguous_placement(nheads, ranks), ranks))
+    best, best_plan = None, None
+    for to, hd in rlb_plans(W, ranks, topology):
+        ob = plan_objective(rank_loads(W, apply_plan(nheads, ranks, to, hd), ranks))
+        if best is None or ob < best:
+            best, best_plan = ob, (to, hd)
+    if not best[0] < ident[0]:
+        return ident, ([-1] * ranks, [-1] * ranks)
+    return best, best_plan
+
+
+def sasa_budget(W, rank_of_head, ranks: int, alpha: float, head_cap: int) -> np.ndarray:
+    """Per-head pair budgets: rank slack s_r = max L - L_r, extra budget
+    floor(alpha * s_r) split evenly over the rank's heads in ascending head id
+    (remainder to the lowest ids); each head's budget is W_h + its share,
+    capped at max(head_cap, W_h)."""
+    L = rank_loads(W, rank_of_head, ranks)
+    lmax = int(L.max())
+    out = np.array([int(x) for x in W], dtype=np.int64)
+    for r in range(ranks):
+        hs = [h for h in range(len(W)) if rank_of_head[h] == r]
+        extra = int(math.floor(float(np.float32(alpha)) * (lmax - int(L[r]))))
+        if not hs or extra <= 0:
+            continue
+        q, rem = divmod(extra, len(hs))
+        for k, h in enumerate(hs):
+            want = int(W[h]) + q + (1 if k < rem else 0)
+            out[h] = min(max(want, int(W[h])), max(head_cap, int(W[h])))
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -344,3 +344,36 @@ def test_trace_covers_every_item_once():
         t0 = tr[:, 4].astype(np.uint64) | (tr[:, 5].astype(np.uint64) << np.uint64(32))
         t1 = tr[:, 6].astype(np.uint64) | (tr[:, 7].astype(np.uint64) << np.uint64(32))
         assert np.all(t1 >= t0) and np.all(t0 > 0)
+
+
+@pytest.mark.parametrize("alpha,cap_scale", [(0.7, 1), (1.0, 1), (0.0, 1), (1.0, 0)])
+def test_topup_with_rank_slack_budgets_bit_exact(alpha, cap_scale):
+    # slack-aware augmentation on virtual ranks: the host planner balances
+    # heads over 3 ranks, the slack budgets go to the device top-up
+    w = small_workload("sasa", 6, 128, (3, 13, 19), (1, 8, 8), 0.6, 1,
+                       amp=(4.0, 0.3, 2.0, 3.5, 0.5, 1.0))
+    q, k, v, qd, kd, vd, buf = setup(w)
+    gpu_reorder(buf, qd, kd, vd)
+    qr = O.reorder(q.float().numpy(), w.grid, w.block)
+    kr = O.reorder(k.float().numpy(), w.grid, w.block)
+    r = O.route_path(qr, kr, w.N, w.BLK, w.scale, w.top_p, w.topk_floor, 0)
+    route(buf, w, scores_in=r["scores32"], aug=0)
+    check_mask_exact(buf, r, w.nB)
+    W = r["head_count"].reshape(-1).tolist()
+    to, hd, roh, st = F.fva_rlb_plan(W, 3, F.FVA_RLB_PAIRS)
+    cap = cap_scale * w.nB * w.nB
+    budgets, _ = F.fva_sasa_budget(W, 3, roh, alpha, cap)
+    assert budgets == O.sasa_budget(W, roh, 3, alpha, cap).tolist()
+    dev_budgets = torch.tensor(budgets, dtype=torch.int64, device="cuda")
+    F.fva_topup(w.B, w.Hh, w.d, buf.grid, dev_budgets, buf.mask(), buf.route_ws,
+                buf.sizes.route_ws_bytes)
+    m2 = O.sasa_topup(r["scores32"], r["mask"], np.array(budgets))
+    c2 = m2.sum(-1)
+    ref = dict(mask=m2, counts=c2, head_count=O.head_workload(m2), queue=O.heaviest_first(c2))
+    check_mask_exact(buf, ref, w.nB)
+    # the augmented mask runs through attention like any other
+    oref = _oracle_attention(w, q, k, v, m2)
+    attn(buf, F.FVA_SCHED_XCD)
+    torch.cuda.synchronize()
+    mx, rel = err_stats(to_np(buf.orr)[:, :, :w.N], oref[:, :, :w.N])
+    assert mx <= MAX_ABS and rel <= MEAN_REL
