@@ -127,9 +127,9 @@ fva_status fva_sizes(const fva_grid* grid, int32_t B, int32_t Hh, int32_t d, fva
   return FVA_OK;
 }
 
-fva_status fva_reorder(const void* src, void* dst, int32_t B, int32_t Hh, int32_t d,
-                       const fva_grid* grid, const int64_t strides[3], int32_t direction,
-                       int32_t layout, hipStream_t stream) {
+fva_status fva_reorder_ex(const void* src, void* dst, int32_t B, int32_t Hh, int32_t d,
+                          const fva_grid* grid, const void* table, const int64_t strides[3],
+                          int32_t direction, int32_t layout, hipStream_t stream) {
   Problem p;
   fva_status st = make_problem(grid, B, Hh, d, &p);
   if (st != FVA_OK) return st;
@@ -146,7 +146,41 @@ fva_status fva_reorder(const void* src, void* dst, int32_t B, int32_t Hh, int32_
                   (long long)strides[i]);
   if (!aligned16(src) || !aligned16(dst)) return fail(FVA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
   if (strides[2] < d) return fail(FVA_ERR_INVALID_ARG, "head stride smaller than d");
-  return launch_reorder(p, src, dst, strides, direction, layout, stream);
+  if (table && tile_count(p) > kMaxTiles)
+    return fail(FVA_ERR_UNSUPPORTED, "%lld tiles exceed %d", (long long)tile_count(p), kMaxTiles);
+  return launch_reorder(p, src, dst, strides, direction, layout, (const int32_t*)table, stream);
+}
+
+fva_status fva_reorder(const void* src, void* dst, int32_t B, int32_t Hh, int32_t d,
+                       const fva_grid* grid, const int64_t strides[3], int32_t direction,
+                       int32_t layout, hipStream_t stream) {
+  return fva_reorder_ex(src, dst, B, Hh, d, grid, nullptr, strides, direction, layout, stream);
+}
+
+fva_status fva_tile_order_bytes(const fva_grid* grid, size_t* bytes) {
+  Problem p;
+  fva_status st = make_problem(grid, 1, 1, 64, &p);
+  if (st != FVA_OK) return st;
+  if (!bytes) return fail(FVA_ERR_INVALID_ARG, "bytes is null");
+  if (tile_count(p) > kMaxTiles)
+    return fail(FVA_ERR_UNSUPPORTED, "%lld tiles exceed %d", (long long)tile_count(p), kMaxTiles);
+  *bytes = tile_table_bytes(tile_count(p));
+  return FVA_OK;
+}
+
+fva_status fva_tile_order(const fva_grid* grid, int32_t order, void* table, size_t table_bytes,
+                          hipStream_t stream) {
+  size_t need = 0;
+  fva_status st = fva_tile_order_bytes(grid, &need);
+  if (st != FVA_OK) return st;
+  if (order != FVA_ORDER_RASTER && order != FVA_ORDER_HILBERT)
+    return fail(FVA_ERR_INVALID_ARG, "order %d", order);
+  if (!table || table_bytes < need)
+    return fail(FVA_ERR_WORKSPACE, "tile table needs %zu bytes", need);
+  if (!aligned16(table)) return fail(FVA_ERR_INVALID_ARG, "table must be 16-byte aligned");
+  Problem p;
+  make_problem(grid, 1, 1, 64, &p);
+  return launch_tile_order(p, order, (int32_t*)table, stream);
 }
 
 fva_status fva_route(const void* qr, const void* kr, int32_t B, int32_t Hh, int32_t d,

@@ -47,7 +47,7 @@ constexpr int kMaxXcdHeads = 4096;
 
 // Kernel launchers (each returns FVA_OK or FVA_ERR_HIP).
 fva_status launch_reorder(const Problem& p, const void* src, void* dst, const int64_t st[3],
-                          int direction, int layout, hipStream_t s);
+                          int direction, int layout, const int32_t* table, hipStream_t s);
 fva_status launch_route(const Problem& p, const void* qr, const void* kr,
                         const fva_route_params& prm, float scale, const fva_mask& m,
                         char* ws, int flags, hipStream_t s);
@@ -59,14 +59,20 @@ fva_status launch_attn(const Problem& p, const void* qr, const void* kr, const v
 
 // ---------------------------------------------------------------- device side
 
-// Reordered position r (< N) -> source token index, for raster order over
-// clipped tiles and raster order inside a tile.  Closed form: every tile frame
-// slab (all tiles with the same tile-t index) covers whole frames, and every
-// tile row inside a slab covers whole rows, so the tile containing r follows
-// from three divisions.
+// Reordered position r (< N) -> source token index.  Tokens inside a tile
+// are always visited in raster order (t, y, x).  Tiles are visited either in
+// raster order (closed form: every tile-frame slab covers whole frames and
+// every tile row inside a slab covers whole rows, so the tile containing r
+// follows from three divisions) or in the order of a tile table (tile_id[k],
+// start[k] = first reordered position of the k-th tile), found by binary
+// search.
 struct BlockOrder {
   int32_t T, H, W, bt, bh, bw;
+  const int32_t* tile_id;  // null: raster tile order
+  const int32_t* start;    // [ntiles + 1]
+  int32_t ntiles;
   __device__ __forceinline__ int64_t src_token(int64_t r) const {
+    if (tile_id) return src_token_table(r);
     const int64_t HW = (int64_t)H * W;
     const int64_t slab = (int64_t)bt * HW;
     const int32_t tt = (int32_t)(r / slab);
@@ -86,6 +92,31 @@ struct BlockOrder {
     const int32_t x = rem - y * sx;
     return ((int64_t)(tt * bt + t) * H + (ty * bh + y)) * W + (tx * bw + x);
   }
+  __device__ __forceinline__ int64_t src_token_table(int64_t r) const {
+    int lo = 0, hi = ntiles;  // start[lo] <= r < start[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((int64_t)start[mid] <= r) lo = mid;
+      else hi = mid;
+    }
+    const int32_t nty = (H + bh - 1) / bh, ntx = (W + bw - 1) / bw;
+    const int32_t id = tile_id[lo];
+    const int32_t tt = id / (nty * ntx), ty = (id / ntx) % nty, tx = id % ntx;
+    const int32_t st = min(bt, T - tt * bt), sy = min(bh, H - ty * bh), sx = min(bw, W - tx * bw);
+    const int32_t o = (int32_t)(r - start[lo]);
+    const int32_t t = o / (sy * sx);
+    const int32_t rem = o - t * (sy * sx);
+    const int32_t y = rem / sx;
+    const int32_t x = rem - y * sx;
+    return ((int64_t)(tt * bt + t) * H + (ty * bh + y)) * W + (tx * bw + x);
+  }
 };
+
+// Tile table (device buffer written by fva_tile_order): header of 4 int32
+// {ntiles, order, 0, 0}, then tile_id[ntiles], then start[ntiles + 1].
+constexpr int kMaxTiles = 8192;
+inline size_t tile_table_bytes(int64_t ntiles) { return 16 + 4 * ntiles + 4 * (ntiles + 1); }
+fva_status launch_tile_order(const Problem& p, int order, int32_t* table, hipStream_t s);
+int64_t tile_count(const Problem& p);
 
 }  // namespace fva

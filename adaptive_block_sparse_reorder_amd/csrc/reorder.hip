@@ -129,11 +129,134 @@ __global__ __launch_bounds__(kThreads) void reorder_tile64_fwd(
   }
 }
 
+// 3-D Hilbert index of cell (x0, x1, x2) on a 2^bits cube, by Skilling's
+// transpose method ("Programming the Hilbert curve", AIP Conf. Proc. 707,
+// 2004): undo excess work from the top bit down, Gray-encode, then read the
+// index off the transposed form by interleaving bits (x0 most significant).
+__device__ uint64_t hilbert3(uint32_t x0, uint32_t x1, uint32_t x2, int bits) {
+  uint32_t X[3] = {x0, x1, x2};
+  const uint32_t M = 1u << (bits - 1);
+  for (uint32_t Q = M; Q > 1; Q >>= 1) {
+    const uint32_t P = Q - 1;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      if (X[i] & Q) {
+        X[0] ^= P;
+      } else {
+        const uint32_t t = (X[0] ^ X[i]) & P;
+        X[0] ^= t;
+        X[i] ^= t;
+      }
+    }
+  }
+  X[1] ^= X[0];
+  X[2] ^= X[1];
+  uint32_t t = 0;
+  for (uint32_t Q = M; Q > 1; Q >>= 1)
+    if (X[2] & Q) t ^= Q - 1;
+  X[0] ^= t;
+  X[1] ^= t;
+  X[2] ^= t;
+  uint64_t h = 0;
+  for (int j = bits - 1; j >= 0; --j)
+#pragma unroll
+    for (int i = 0; i < 3; ++i) h = (h << 1) | ((X[i] >> j) & 1u);
+  return h;
+}
+
+// One workgroup: order the tiles (raster or Hilbert over tile coordinates
+// (tile-frame, tile-row, tile-column) on the bounding 2^m cube, out-of-grid
+// cells skipped), then prefix-sum the clipped tile sizes into start[].
+constexpr int kOrderThreads = 1024;
+
+__global__ __launch_bounds__(kOrderThreads) void tile_order_kernel(BlockOrder g, int order,
+                                                                   int64_t N, int32_t* table) {
+  __shared__ uint64_t keys[kMaxTiles];
+  __shared__ int32_t wsum[kOrderThreads / 64];
+  const int nt = (g.T + g.bt - 1) / g.bt, ny = (g.H + g.bh - 1) / g.bh, nx = (g.W + g.bw - 1) / g.bw;
+  const int ntiles = nt * ny * nx;
+  int P = 1;
+  while (P < ntiles) P <<= 1;
+  int bits = 1;
+  while ((1 << bits) < max(nt, max(ny, nx))) ++bits;
+  for (int i = threadIdx.x; i < P; i += kOrderThreads) {
+    uint64_t key = ~0ull;
+    if (i < ntiles) {
+      const uint32_t tt = i / (ny * nx), ty = (i / nx) % ny, tx = i % nx;
+      const uint64_t h = order == FVA_ORDER_HILBERT ? hilbert3(tt, ty, tx, bits) : (uint64_t)i;
+      key = (h << 13) | (uint64_t)i;
+    }
+    keys[i] = key;
+  }
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int q = threadIdx.x; q < P / 2; q += kOrderThreads) {
+        const int i = 2 * j * (q / j) + (q % j), l = i + j;
+        const uint64_t a = keys[i], b = keys[l];
+        if ((a > b) == ((i & k) == 0)) { keys[i] = b; keys[l] = a; }
+      }
+      __syncthreads();
+    }
+  int32_t* tile_id = table + 4;
+  int32_t* start = tile_id + ntiles;
+  // each thread owns a contiguous run of tiles; exclusive scan of their sizes
+  const int per = (ntiles + kOrderThreads - 1) / kOrderThreads;
+  const int k0 = threadIdx.x * per;
+  int local = 0;
+  for (int k = k0; k < min(ntiles, k0 + per); ++k) {
+    const int id = (int)(keys[k] & 8191u);
+    tile_id[k] = id;
+    const int tt = id / (ny * nx), ty = (id / nx) % ny, tx = id % nx;
+    local += min(g.bt, g.T - tt * g.bt) * min(g.bh, g.H - ty * g.bh) * min(g.bw, g.W - tx * g.bw);
+  }
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  int x = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int run = x - local;
+  for (int w = 0; w < wave; ++w) run += wsum[w];
+  for (int k = k0; k < min(ntiles, k0 + per); ++k) {
+    start[k] = run;
+    const int id = tile_id[k];
+    const int tt = id / (ny * nx), ty = (id / nx) % ny, tx = id % nx;
+    run += min(g.bt, g.T - tt * g.bt) * min(g.bh, g.H - ty * g.bh) * min(g.bw, g.W - tx * g.bw);
+  }
+  if (threadIdx.x == 0) {
+    start[ntiles] = (int32_t)N;
+    table[0] = ntiles;
+    table[1] = order;
+    table[2] = 0;
+    table[3] = 0;
+  }
+}
+
 }  // namespace
 
+int64_t tile_count(const Problem& p) {
+  return (int64_t)((p.T + p.bt - 1) / p.bt) * ((p.H + p.bh - 1) / p.bh) * ((p.W + p.bw - 1) / p.bw);
+}
+
+fva_status launch_tile_order(const Problem& p, int order, int32_t* table, hipStream_t s) {
+  BlockOrder g{p.T, p.H, p.W, p.bt, p.bh, p.bw, nullptr, nullptr, 0};
+  hipLaunchKernelGGL(tile_order_kernel, dim3(1), dim3(kOrderThreads), 0, s, g, order, p.N, table);
+  return hip_fail(hipGetLastError(), "tile order launch");
+}
+
 fva_status launch_reorder(const Problem& p, const void* src, void* dst, const int64_t st[3],
-                          int direction, int layout, hipStream_t s) {
-  BlockOrder bo{p.T, p.H, p.W, p.bt, p.bh, p.bw};
+                          int direction, int layout, const int32_t* table, hipStream_t s) {
+  BlockOrder bo{p.T, p.H, p.W, p.bt, p.bh, p.bw, nullptr, nullptr, 0};
+  if (table) {
+    const int64_t nt = tile_count(p);
+    bo.tile_id = table + 4;
+    bo.start = table + 4 + nt;
+    bo.ntiles = (int32_t)nt;
+  }
   const uint16_t* in = (const uint16_t*)src;
   uint16_t* out = (uint16_t*)dst;
   if (direction == FVA_FORWARD && layout == FVA_LAYOUT_ROWS) {

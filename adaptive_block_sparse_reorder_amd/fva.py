@@ -36,6 +36,8 @@ FVA_INVERSE = 1
 FVA_LAYOUT_ROWS = 0
 FVA_LAYOUT_V64 = 1
 FVA_LAYOUT_K64 = 2
+FVA_ORDER_RASTER = 0
+FVA_ORDER_HILBERT = 1
 FVA_RLB_PAIRS = 0
 FVA_RLB_RING = 1
 FVA_RLB_MAX_PAIR_RANKS = 12
@@ -101,6 +103,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fva_sparse_attn.argtypes = [P, P, P, P, I32, I32, I32, ctypes.POINTER(fva_grid),
                                     ctypes.POINTER(fva_mask), F, I32, P, SZ, P, P]
     lib.fva_dense_attn.argtypes = [P, P, P, P, I32, I32, I32, ctypes.POINTER(fva_grid), F, P]
+    lib.fva_reorder_ex.argtypes = [P, P, I32, I32, I32, ctypes.POINTER(fva_grid), P,
+                                   ctypes.POINTER(ctypes.c_int64), I32, I32, P]
+    lib.fva_tile_order_bytes.argtypes = [ctypes.POINTER(fva_grid), ctypes.POINTER(ctypes.c_size_t)]
+    lib.fva_tile_order.argtypes = [ctypes.POINTER(fva_grid), I32, P, SZ, P]
     PI32 = ctypes.POINTER(ctypes.c_int32)
     PI64 = ctypes.POINTER(ctypes.c_int64)
     lib.fva_rlb_plan.argtypes = [PI32, I32, I32, I32, PI32, PI32, PI32,
@@ -109,7 +115,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fva_topup.argtypes = [I32, I32, I32, ctypes.POINTER(fva_grid), P,
                               ctypes.POINTER(fva_mask), P, SZ, P]
     for fn in ("fva_sizes", "fva_reorder", "fva_route", "fva_route_flags", "fva_sparse_attn",
-               "fva_dense_attn", "fva_rlb_plan", "fva_sasa_budget", "fva_topup"):
+               "fva_dense_attn", "fva_rlb_plan", "fva_sasa_budget", "fva_topup",
+               "fva_reorder_ex", "fva_tile_order_bytes", "fva_tile_order"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.fva_status_string.argtypes = [ctypes.c_int]
     lib.fva_status_string.restype = ctypes.c_char_p
@@ -164,6 +171,37 @@ def fva_reorder(src, dst, B: int, Hh: int, d: int, grid: fva_grid, strides: Sequ
     st = (ctypes.c_int64 * 3)(*[int(s) for s in strides])
     _check(lib.fva_reorder(_ptr(src), _ptr(dst), B, Hh, d, ctypes.byref(grid), st, direction,
                            layout, _stream(stream)), "fva_reorder")
+
+
+def fva_reorder_ex(src, dst, B: int, Hh: int, d: int, grid: fva_grid, table,
+                   strides: Sequence[int], direction: int = FVA_FORWARD,
+                   layout: int = FVA_LAYOUT_ROWS, stream=None):
+    lib = load_library()
+    st = (ctypes.c_int64 * 3)(*[int(s) for s in strides])
+    _check(lib.fva_reorder_ex(_ptr(src), _ptr(dst), B, Hh, d, ctypes.byref(grid), _ptr(table), st,
+                              direction, layout, _stream(stream)), "fva_reorder_ex")
+
+
+def fva_tile_order_bytes(grid: fva_grid) -> int:
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib.fva_tile_order_bytes(ctypes.byref(grid), ctypes.byref(n)), "fva_tile_order_bytes")
+    return int(n.value)
+
+
+def fva_tile_order(grid: fva_grid, order: int, table, table_bytes: int, stream=None):
+    lib = load_library()
+    _check(lib.fva_tile_order(ctypes.byref(grid), order, _ptr(table), table_bytes,
+                              _stream(stream)), "fva_tile_order")
+
+
+def tile_table(grid: fva_grid, order: int = FVA_ORDER_HILBERT, device="cuda", stream=None):
+    """Allocate (torch) and fill a device tile table."""
+    import torch
+    nbytes = fva_tile_order_bytes(grid)
+    t = torch.empty((nbytes + 3) // 4, dtype=torch.int32, device=device)
+    fva_tile_order(grid, order, t, nbytes, stream)
+    return t
 
 
 def fva_route(qr, kr, B: int, Hh: int, d: int, grid: fva_grid, params: fva_route_params,
@@ -302,14 +340,18 @@ def token_strides(x) -> Sequence[int]:
 
 def forward(buf: Buffers, q, k, v, top_p: float, topk_floor: int, aug_budget: int = 0,
             scale: float = 0.0, route_flags: int = 0, attn_flags: int = FVA_SCHED_XCD,
-            stream=None):
+            stream=None, table=None):
     """One pass of the hot path: reorder Q (rows), K (k64), V (v64) -> route -> block-sparse
     attention -> inverse reorder.  Inputs [B, N, Hh, d] bf16 on the device;
-    the result lands in buf.out."""
+    the result lands in buf.out.  `table`: a device tile table from
+    fva_tile_order (None = raster tile order)."""
     g, B, Hh, d = buf.grid, buf.B, buf.Hh, buf.d
-    fva_reorder(q, buf.qr, B, Hh, d, g, token_strides(q), FVA_FORWARD, FVA_LAYOUT_ROWS, stream)
-    fva_reorder(k, buf.kr, B, Hh, d, g, token_strides(k), FVA_FORWARD, FVA_LAYOUT_K64, stream)
-    fva_reorder(v, buf.vt, B, Hh, d, g, token_strides(v), FVA_FORWARD, FVA_LAYOUT_V64, stream)
+    fva_reorder_ex(q, buf.qr, B, Hh, d, g, table, token_strides(q), FVA_FORWARD,
+                   FVA_LAYOUT_ROWS, stream)
+    fva_reorder_ex(k, buf.kr, B, Hh, d, g, table, token_strides(k), FVA_FORWARD,
+                   FVA_LAYOUT_K64, stream)
+    fva_reorder_ex(v, buf.vt, B, Hh, d, g, table, token_strides(v), FVA_FORWARD,
+                   FVA_LAYOUT_V64, stream)
     prm = fva_route_params(top_p, topk_floor, aug_budget, scale, 0)
     m = buf.mask()
     fva_route(buf.qr, buf.kr, B, Hh, d, g, prm, m, buf.route_ws, buf.sizes.route_ws_bytes,
@@ -317,8 +359,8 @@ def forward(buf: Buffers, q, k, v, top_p: float, topk_floor: int, aug_budget: in
     fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, B, Hh, d, g, m, scale, attn_flags,
                     buf.attn_ws, buf.sizes.attn_ws_bytes,
                     buf.trace if (attn_flags & FVA_TRACE) else None, stream)
-    fva_reorder(buf.orr, buf.out, B, Hh, d, g, token_strides(buf.out), FVA_INVERSE,
-                FVA_LAYOUT_ROWS, stream)
+    fva_reorder_ex(buf.orr, buf.out, B, Hh, d, g, table, token_strides(buf.out), FVA_INVERSE,
+                   FVA_LAYOUT_ROWS, stream)
     return buf.out
 
 

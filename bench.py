@@ -247,6 +247,43 @@ def main():
             lam[name] = lambda_cu(buf.trace.cpu().numpy().view(np.uint32), int(buf.sizes.rows))
         extras["lambda_cu"] = lam
 
+    if not args.no_extras:
+        # the same step with the tile order along a 3-D Hilbert curve
+        table = F.tile_table(g, F.FVA_ORDER_HILBERT)
+        ev.clear()
+        for _ in range(2):
+            F.forward(buf, qd, kd, vd, w.top_p, w.topk_floor, w.aug_budget, attn_flags=args.sched,
+                      table=table)
+        hev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        hev[0].record(stream)
+        for x, dst, lay in ((qd, buf.qr, F.FVA_LAYOUT_ROWS), (kd, buf.kr, F.FVA_LAYOUT_K64),
+                            (vd, buf.vt, F.FVA_LAYOUT_V64)):
+            F.fva_reorder_ex(x, dst, w.B, w.Hh, w.d, g, table, F.token_strides(x),
+                             F.FVA_FORWARD, lay)
+        hev[1].record(stream)
+        F.fva_route(buf.qr, buf.kr, w.B, w.Hh, w.d, g, prm, m, buf.route_ws,
+                    buf.sizes.route_ws_bytes, 0)
+        hev[2].record(stream)
+        F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, g, m, 0.0,
+                          args.sched, buf.attn_ws, buf.sizes.attn_ws_bytes, None)
+        hev[3].record(stream)
+        F.fva_reorder_ex(buf.orr, buf.out, w.B, w.Hh, w.d, g, table, F.token_strides(buf.out),
+                         F.FVA_INVERSE)
+        hev[4].record(stream)
+        torch.cuda.synchronize()
+        hnnz = int(buf.row_count.sum().item())
+        extras["hilbert_order"] = {
+            "density_mean": round(hnnz / (w.B * w.Hh * w.nB ** 2), 4),
+            "density_mean_raster": round(nnz / (w.B * w.Hh * w.nB ** 2), 4),
+            "reorder_qkv_ms": round(hev[0].elapsed_time(hev[1]), 4),
+            "route_ms": round(hev[1].elapsed_time(hev[2]), 4),
+            "sparse_attn_ms": round(hev[2].elapsed_time(hev[3]), 4),
+            "unreorder_ms": round(hev[3].elapsed_time(hev[4]), 4),
+        }
+        # restore the raster-order state for what follows
+        step(False)
+        torch.cuda.synchronize()
+
     # runtime load balancing on 8 virtual ranks from the realized workloads
     hc = buf.head_count.cpu().numpy().astype(np.int64).tolist()
     rlb = {}

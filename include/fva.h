@@ -151,6 +151,32 @@ fva_status fva_reorder(const void* src, void* dst, int32_t B, int32_t Hh, int32_
                        const fva_grid* grid, const int64_t strides[3],
                        int32_t direction, int32_t layout, hipStream_t stream);
 
+/* Tile orders for the block organization (section 3.1: blocks are ordered
+ * along a Hilbert curve so that spatially adjacent tokens fall into nearby
+ * blocks across scales). */
+#define FVA_ORDER_RASTER 0   /* tiles in raster order (what fva_reorder uses)   */
+#define FVA_ORDER_HILBERT 1  /* tiles by their 3-D Hilbert index over (tile
+                                frame, tile row, tile column) on the bounding
+                                2^m cube, out-of-grid cells skipped          */
+
+/* Bytes of the device tile table for `grid` (at most 8192 tiles). */
+fva_status fva_tile_order_bytes(const fva_grid* grid, size_t* bytes);
+
+/* Writes the tile table of `order` for `grid` into the DEVICE buffer `table`
+ * (fva_tile_order_bytes() bytes): {ntiles, order, 0, 0} then the raster id of
+ * the k-th tile, then the first reordered position of the k-th tile
+ * (ntiles + 1 entries, the last = N).  Tokens inside a tile stay in raster
+ * order.                                                                    */
+fva_status fva_tile_order(const fva_grid* grid, int32_t order, void* table, size_t table_bytes,
+                          hipStream_t stream);
+
+/* fva_reorder with the tile order taken from a table written by
+ * fva_tile_order (DEVICE pointer); table = NULL is raster order.  All other
+ * arguments and layouts are as for fva_reorder.                             */
+fva_status fva_reorder_ex(const void* src, void* dst, int32_t B, int32_t Hh, int32_t d,
+                          const fva_grid* grid, const void* table, const int64_t strides[3],
+                          int32_t direction, int32_t layout, hipStream_t stream);
+
 /* Sparse-routing frontend (sections 2 and 3.1; top-up section 3.3).
  * qr: `rows` bf16, kr: `k64` bf16.  For every row (b, h, i):
  *   1. unless FVA_ROUTE_SCORES_IN: qbar, kbar = mean of each block's real

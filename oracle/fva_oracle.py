@@ -10,8 +10,10 @@ reordering beyond what each step's definition states.
 
 Steps and the passages they follow (all on the FVAttn page):
   block_order / reorder / unreorder  section 3.1, video-aware block organization
-                                     (reading: raster order over clipped tiles,
-                                     raster order inside a tile, tail padding)
+                                     (reading: raster or Hilbert order over clipped
+                                     tiles, raster order inside a tile, tail padding)
+  hilbert_index_3d / tile_order      section 3.1 (blocks ordered along a Hilbert
+                                     curve), Skilling's transpose method
   pool                               section 3.1, block similarities from pooled Q/K
   block_scores                       section 2 (importance score per head, q-block,
                                      k-block) and section 3.1 (pooled Q/K)
@@ -49,26 +51,84 @@ import numpy as np
 # Video-aware block organization (section 3.1)
 # --------------------------------------------------------------------------
 
-def block_order(T: int, H: int, W: int, bt: int, bh: int, bw: int) -> np.ndarray:
+def hilbert_index_3d(c0: int, c1: int, c2: int, bits: int) -> int:
+    """Index of cell (c0, c1, c2) along the 3-D Hilbert curve of a 2^bits cube,
+    by the transpose method of J. Skilling, "Programming the Hilbert curve"
+    (AIP Conf. Proc. 707, 2004): from the top bit down, for each lower-bit
+    mask either invert the low bits of the first coordinate (bit set) or
+    exchange low bits between the first coordinate and this one (bit clear);
+    then Gray-encode across coordinates, apply the final correction, and read
+    the index by interleaving bits from the top, first coordinate first."""
+    x = [int(c0), int(c1), int(c2)]
+    top = 1 << (bits - 1)
+    q = top
+    while q > 1:
+        low = q - 1
+        for i in range(3):
+            if x[i] & q:
+                x[0] ^= low
+            else:
+                swap = (x[0] ^ x[i]) & low
+                x[0] ^= swap
+                x[i] ^= swap
+        q >>= 1
+    for i in range(1, 3):
+        x[i] ^= x[i - 1]
+    corr = 0
+    q = top
+    while q > 1:
+        if x[2] & q:
+            corr ^= q - 1
+        q >>= 1
+    x = [v ^ corr for v in x]
+    h = 0
+    for j in range(bits - 1, -1, -1):
+        for i in range(3):
+            h = (h << 1) | ((x[i] >> j) & 1)
+    return h
+
+
+def tile_grid(T, H, W, bt, bh, bw) -> Tuple[int, int, int]:
+    return -(-T // bt), -(-H // bh), -(-W // bw)
+
+
+def tile_order(T, H, W, bt, bh, bw, order: str = "raster") -> List[int]:
+    """Tile raster ids (tile-frame, tile-row, tile-column raster numbering) in
+    visiting order: 'raster', or 'hilbert' = ascending Hilbert index of the
+    tile coordinates on the bounding 2^m cube (cells outside the grid do not
+    exist and are skipped)."""
+    nt, ny, nx = tile_grid(T, H, W, bt, bh, bw)
+    ids = list(range(nt * ny * nx))
+    if order == "raster":
+        return ids
+    if order != "hilbert":
+        raise ValueError(order)
+    bits = max(1, int(math.ceil(math.log2(max(nt, ny, nx)))))
+    key = {i: hilbert_index_3d(i // (ny * nx), (i // nx) % ny, i % nx, bits) for i in ids}
+    return sorted(ids, key=lambda i: key[i])
+
+
+def block_order(T: int, H: int, W: int, bt: int, bh: int, bw: int,
+                order: str = "raster") -> np.ndarray:
     """Reordered position r -> source token index, length N = T*H*W.
 
-    Tiles of bt x bh x bw tokens are visited in raster order (tile t, then tile
-    row, then tile column); tiles at the grid edge are clipped.  Inside a tile
-    the tokens are visited in raster order (t, y, x).  Source token index of
-    (t, y, x) is (t*H + y)*W + x.
+    Tiles of bt x bh x bw tokens are visited in tile order (raster by default:
+    tile t, then tile row, then tile column; or Hilbert); tiles at the grid
+    edge are clipped.  Inside a tile the tokens are visited in raster order
+    (t, y, x).  Source token index of (t, y, x) is (t*H + y)*W + x.
     """
+    nt, ny, nx = tile_grid(T, H, W, bt, bh, bw)
     out: List[np.ndarray] = []
-    for t0 in range(0, T, bt):
-        for y0 in range(0, H, bh):
-            for x0 in range(0, W, bw):
-                ts = np.arange(t0, min(t0 + bt, T))
-                ys = np.arange(y0, min(y0 + bh, H))
-                xs = np.arange(x0, min(x0 + bw, W))
-                tok = (ts[:, None, None] * H + ys[None, :, None]) * W + xs[None, None, :]
-                out.append(tok.reshape(-1))
-    order = np.concatenate(out).astype(np.int64)
-    assert order.shape[0] == T * H * W
-    return order
+    for tid in tile_order(T, H, W, bt, bh, bw, order):
+        t0, y0, x0 = (tid // (ny * nx)) * bt, ((tid // nx) % ny) * bh, (tid % nx) * bw
+        ts = np.arange(t0, min(t0 + bt, T))
+        ys = np.arange(y0, min(y0 + bh, H))
+        xs = np.arange(x0, min(x0 + bw, W))
+        tok = (ts[:, None, None] * H + ys[None, :, None]) * W + xs[None, None, :]
+        out.append(tok.reshape(-1))
+    result = np.concatenate(out).astype(np.int64)
+    assert result.shape[0] == T * H * W
+    return result
 
 
 def sizes(T, H, W, bt, bh, bw) -> Tuple[int, int, int, int]:
@@ -79,24 +139,26 @@ def sizes(T, H, W, bt, bh, bw) -> Tuple[int, int, int, int]:
     return N, BLK, nB, nB * BLK
 
 
-def reorder(x: np.ndarray, grid: Sequence[int], block: Sequence[int]) -> np.ndarray:
+def reorder(x: np.ndarray, grid: Sequence[int], block: Sequence[int],
+            order: str = "raster") -> np.ndarray:
     """[B, N, Hh, d] -> [B, Hh, Npad, d] in block order, pad rows zero.
     Pure data movement: the dtype is kept."""
     N, BLK, nB, Npad = sizes(*grid, *block)
     B, n, Hh, d = x.shape
     assert n == N
-    order = block_order(*grid, *block)
+    order = block_order(*grid, *block, order=order)
     y = np.zeros((B, Hh, Npad, d), dtype=x.dtype)
     y[:, :, :N, :] = np.transpose(x[:, order, :, :], (0, 2, 1, 3))
     return y
 
 
-def unreorder(y: np.ndarray, grid: Sequence[int], block: Sequence[int]) -> np.ndarray:
+def unreorder(y: np.ndarray, grid: Sequence[int], block: Sequence[int],
+              order: str = "raster") -> np.ndarray:
     """[B, Hh, Npad, d] -> [B, N, Hh, d]; padded rows are dropped."""
     N, BLK, nB, Npad = sizes(*grid, *block)
     B, Hh, npad, d = y.shape
     assert npad == Npad
-    order = block_order(*grid, *block)
+    order = block_order(*grid, *block, order=order)
     x = np.empty((B, N, Hh, d), dtype=y.dtype)
     x[:, order, :, :] = np.transpose(y[:, :, :N, :], (0, 2, 1, 3))
     return x
@@ -413,12 +475,12 @@ def route_path(qr, kr, N, BLK, scale, top_p, topk, aug_budget=0) -> Dict[str, np
                 head_count=head_workload(mask_aug), queue=heaviest_first(counts_aug))
 
 
-def forward(q, k, v, grid, block, top_p, topk, aug_budget=0, scale=None):
+def forward(q, k, v, grid, block, top_p, topk, aug_budget=0, scale=None, order="raster"):
     """Full path on [B, N, Hh, d] inputs; returns (O [B, N, Hh, d] f64, route dict)."""
     N, BLK, nB, Npad = sizes(*grid, *block)
     d = q.shape[-1]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    qr, kr, vr = (reorder(x, grid, block) for x in (q, k, v))
+    qr, kr, vr = (reorder(x, grid, block, order) for x in (q, k, v))
     r = route_path(qr, kr, N, BLK, scale, top_p, topk, aug_budget)
     orr = sparse_attention(qr, kr, vr, r["mask"], N, BLK, scale)
-    return unreorder(orr, grid, block), r
+    return unreorder(orr, grid, block, order), r

@@ -377,3 +377,59 @@ def test_topup_with_rank_slack_budgets_bit_exact(alpha, cap_scale):
     torch.cuda.synchronize()
     mx, rel = err_stats(to_np(buf.orr)[:, :, :w.N], oref[:, :, :w.N])
     assert mx <= MAX_ABS and rel <= MEAN_REL
+
+
+# ----------------------------------------------------------------- Hilbert tile order
+
+@pytest.mark.parametrize("entry", SMALL, ids=[e[0] for e in SMALL])
+def test_hilbert_tile_table_and_reorder_bit_exact(entry):
+    w = _wl(entry)
+    q, k, v, qd, kd, vd, buf = setup(w)
+    table = F.tile_table(buf.grid, F.FVA_ORDER_HILBERT)
+    torch.cuda.synchronize()
+    nt = int(np.prod(O.tile_grid(*w.grid, *w.block)))
+    t = table.cpu().numpy()
+    assert t[0] == nt and t[1] == F.FVA_ORDER_HILBERT
+    want_ids = O.tile_order(*w.grid, *w.block, "hilbert")
+    assert t[4:4 + nt].tolist() == want_ids
+    order = O.block_order(*w.grid, *w.block, "hilbert")
+    starts = t[4 + nt:4 + 2 * nt + 1]
+    assert starts[-1] == w.N and np.all(np.diff(starts) > 0)
+    g = buf.grid
+    F.fva_reorder_ex(qd, buf.qr, w.B, w.Hh, w.d, g, table, F.token_strides(qd))
+    F.fva_reorder_ex(kd, buf.kr, w.B, w.Hh, w.d, g, table, F.token_strides(kd), F.FVA_FORWARD,
+                     F.FVA_LAYOUT_K64)
+    F.fva_reorder_ex(vd, buf.vt, w.B, w.Hh, w.d, g, table, F.token_strides(vd), F.FVA_FORWARD,
+                     F.FVA_LAYOUT_V64)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(buf.qr), O.reorder(q.view(torch.int16).numpy(), w.grid, w.block,
+                                                  "hilbert"))
+    assert np.array_equal(bits(buf.kr), k64_expected(
+        O.reorder(k.view(torch.int16).numpy(), w.grid, w.block, "hilbert")))
+    assert np.array_equal(bits(buf.vt), v64_expected(
+        O.reorder(v.view(torch.int16).numpy(), w.grid, w.block, "hilbert")))
+    out = torch.empty_like(qd)
+    F.fva_reorder_ex(buf.qr, out, w.B, w.Hh, w.d, g, table, F.token_strides(out), F.FVA_INVERSE)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu().view(torch.int16), q.view(torch.int16))
+    # the raster table reproduces the closed-form raster order
+    rt = F.tile_table(buf.grid, F.FVA_ORDER_RASTER)
+    F.fva_reorder_ex(qd, buf.qr, w.B, w.Hh, w.d, g, rt, F.token_strides(qd))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(buf.qr), O.reorder(q.view(torch.int16).numpy(), w.grid, w.block))
+
+
+def test_full_path_with_hilbert_order():
+    w = SMALL[3][1]
+    q, k, v, qd, kd, vd, buf = setup(w)
+    table = F.tile_table(buf.grid, F.FVA_ORDER_HILBERT)
+    F.forward(buf, qd, kd, vd, w.top_p, w.topk_floor, w.aug_budget, table=table)
+    torch.cuda.synchronize()
+    o_ref, r = O.forward(q.float().numpy(), k.float().numpy(), v.float().numpy(), w.grid,
+                         w.block, w.top_p, w.topk_floor, w.aug_budget, order="hilbert")
+    got = unpack_bitmask(buf.bitmask, w.nB)
+    differ = (got != r["mask"].reshape(-1, w.nB)).any(axis=1)
+    assert differ.sum() == 0 or np.all(r["margin"].reshape(-1)[differ] < 1e-4)
+    if differ.sum() == 0:
+        mx, rel = err_stats(to_np(buf.out), o_ref)
+        assert mx <= MAX_ABS and rel <= MEAN_REL

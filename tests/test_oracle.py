@@ -372,3 +372,46 @@ def test_sparse_output_equals_dense_on_selected_keys_only():
     v = torch.from_numpy(vr[0, 0, keys])[None, None]
     ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=0.3)[0, 0].numpy()
     assert np.abs(out[0, 0, 8:16] - ref).max() < 1e-12
+
+
+# ----------------------------------------------------------------- Hilbert order
+
+@pytest.mark.parametrize("bits", [1, 2, 3])
+def test_hilbert_curve_is_a_face_adjacent_walk_of_the_cube(bits):
+    n = 1 << bits
+    cells = sorted(((t, y, x) for t in range(n) for y in range(n) for x in range(n)),
+                   key=lambda c: O.hilbert_index_3d(*c, bits))
+    idx = sorted(O.hilbert_index_3d(*c, bits) for c in cells)
+    assert idx == list(range(n ** 3))                      # a bijection onto 0..n^3-1
+    for a, b in zip(cells[:-1], cells[1:]):
+        assert sum(abs(u - v) for u, v in zip(a, b)) == 1  # consecutive cells share a face
+    # self-similar: every aligned half-size sub-cube is one contiguous run
+    h = n // 2
+    if h >= 1:
+        for k in range(8):
+            run = cells[k * h ** 3:(k + 1) * h ** 3]
+            assert len({(c[0] // h, c[1] // h, c[2] // h) for c in run}) == 1
+
+
+def test_hilbert_tile_order_restricts_the_cube_walk():
+    # a 3 x 6 x 5 tile grid inside the 8^3 cube: in-grid cells in cube-walk order
+    T, H, W, bt, bh, bw = 3, 48, 80, 1, 8, 16
+    nt, ny, nx = O.tile_grid(T, H, W, bt, bh, bw)
+    assert (nt, ny, nx) == (3, 6, 5)
+    walk = sorted(((t, y, x) for t in range(8) for y in range(8) for x in range(8)),
+                  key=lambda c: O.hilbert_index_3d(*c, 3))
+    want = [(t * ny + y) * nx + x for (t, y, x) in walk if t < nt and y < ny and x < nx]
+    assert O.tile_order(T, H, W, bt, bh, bw, "hilbert") == want
+    o = O.block_order(T, H, W, bt, bh, bw, "hilbert")
+    assert np.array_equal(np.sort(o), np.arange(T * H * W))
+
+
+def test_hilbert_reorder_roundtrip_and_dense_equivalence():
+    grid, block = (3, 13, 19), (1, 8, 8)
+    N = 3 * 13 * 19
+    rng = np.random.default_rng(13)
+    q, k, v = (rng.standard_normal((1, N, 2, 16)).astype(np.float32) for _ in range(3))
+    y = O.reorder(q, grid, block, "hilbert")
+    assert np.array_equal(O.unreorder(y, grid, block, "hilbert"), q)
+    o, _ = O.forward(q, k, v, grid, block, top_p=1.0, topk=0, order="hilbert")
+    assert np.abs(o - _sdpa64(q, k, v, 0.25)).max() < 1e-11

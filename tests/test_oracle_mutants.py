@@ -55,6 +55,14 @@ MUTANTS = [
      ["test_sparse_output_equals_dense_on_selected_keys_only"]),
     ("queue lightest-first", "key=lambda t: (-int(flat[t]), t)",
      "key=lambda t: (int(flat[t]), t)", ["test_heaviest_first_order"]),
+    ("Hilbert without Gray encoding", "    for i in range(1, 3):\n        x[i] ^= x[i - 1]\n",
+     "", [("test_hilbert_curve_is_a_face_adjacent_walk_of_the_cube", {"bits": 3})]),
+    ("Hilbert exchange replaced by inversion",
+     "                swap = (x[0] ^ x[i]) & low\n                x[0] ^= swap\n                x[i] ^= swap",
+     "                x[0] ^= low",
+     [("test_hilbert_curve_is_a_face_adjacent_walk_of_the_cube", {"bits": 3})]),
+    ("Hilbert tiles in raster order", "    return sorted(ids, key=lambda i: key[i])",
+     "    return ids", ["test_hilbert_tile_order_restricts_the_cube_walk"]),
 ]
 
 
@@ -70,10 +78,12 @@ def _mutant_module(old, new):
 @pytest.mark.parametrize("name,old,new,catchers", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pin_catches_mutant(name, old, new, catchers, monkeypatch):
     monkeypatch.setattr(T, "O", _mutant_module(old, new))
+    # every catcher passes on the real oracle (so a catch is the mutant's doing)
     caught = []
-    for t in catchers:
+    for c in catchers:
+        t, kw = (c, {}) if isinstance(c, str) else c
         try:
-            getattr(T, t)()
-        except Exception:
+            getattr(T, t)(**kw)
+        except AssertionError:
             caught.append(t)
     assert caught, f"no pin caught mutant: {name}"
