@@ -67,6 +67,10 @@ RouteWs route_ws_layout(const Problem& p) {
   off = align256(off + (size_t)p.rows * p.d * sizeof(float));
   L.thresh_off = off;
   off = align256(off + (size_t)p.B * p.Hh * sizeof(uint64_t));
+  L.tstate_off = off;
+  off = align256(off + (size_t)p.B * p.Hh * 24);
+  L.thist_off = off;
+  off = align256(off + (size_t)p.B * p.Hh * 256 * sizeof(uint32_t));
   L.qtmp_row_off = off;
   off = align256(off + (size_t)p.rows * sizeof(int32_t));
   L.qtmp_rank_off = off;

@@ -35,6 +35,8 @@ struct RouteWs {
   size_t qbar_off;      // float [rows, d]
   size_t kbar_off;      // float [rows, d]
   size_t thresh_off;    // uint64 [B*Hh] top-up threshold keys
+  size_t tstate_off;    // [B*Hh] top-up radix-select state (16 bytes each)
+  size_t thist_off;     // uint32 [B*Hh, 256] top-up radix-select histograms
   size_t qtmp_row_off;  // int32 [rows] queue sort: rows in chunk-sorted order
   size_t qtmp_rank_off; // int32 [rows] queue sort: rank inside a run of equal counts
   size_t qhist_off;     // int32 [ceil(rows/1024), nB+1] queue sort: run lengths -> offsets

@@ -317,64 +317,83 @@ __device__ __forceinline__ uint64_t pair_key(float s, int i, int j) {
   return ((uint64_t)(~order_key(s)) << 30) | ((uint64_t)i << 15) | (uint64_t)j;
 }
 
-constexpr int kSelThreads = 1024;
+// Exact selection of the need-th smallest priority key among a head's
+// unselected pairs (need = budget - W_h), by an 8-pass radix select over the
+// 62-bit keys (digits of 8 bits from the top, the last of 6).  Each pass is
+// a sliced histogram (many workgroups per head, LDS histograms merged with
+// global atomics) and a per-head pick of the digit where the running count
+// reaches need.  thresh[bh] is an exclusive bound: pairs with key < thresh
+// are added; 0 means none, ~0 means every unselected pair.
+struct TopupState {
+  uint64_t prefix;
+  int64_t need;
+  int32_t mode;  // 0 none, 1 select, 2 all
+  int32_t pad;
+};
+constexpr int kSelSlices = 32;
 
-// One workgroup per head: exact radix select (8-bit digits, 8 passes) of the
-// need-th smallest priority key among unselected pairs, need = budget - W_h
-// with the budget per head (budgets[bh]) or shared (budget).  thresh[bh] is an
-// exclusive bound: pairs with key < thresh are added; 0 means none.
-__global__ __launch_bounds__(kSelThreads) void topup_select_kernel(
-    const float* __restrict__ S, const uint32_t* __restrict__ bitmask,
-    const int32_t* __restrict__ head_count, int nB, int words, int64_t budget,
-    const int64_t* __restrict__ budgets, uint64_t* __restrict__ thresh) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint64_t s_prefix;
-  __shared__ int64_t s_need;
-  const int64_t bh = blockIdx.x;
+__global__ void topup_init_kernel(const int32_t* __restrict__ head_count, int nB, int64_t budget,
+                                  const int64_t* __restrict__ budgets, int nheads,
+                                  TopupState* __restrict__ st, uint32_t* __restrict__ ghist,
+                                  uint64_t* __restrict__ thresh) {
+  const int bh = blockIdx.x;
+  for (int b = threadIdx.x; b < 256; b += blockDim.x) ghist[bh * 256 + b] = 0u;
+  if (threadIdx.x != 0) return;
   const int64_t pairs = (int64_t)nB * nB;
   const int64_t W = head_count[bh];
-  int64_t need = (budgets ? budgets[bh] : budget) - W;
-  if (need <= 0) {
-    if (threadIdx.x == 0) thresh[bh] = 0ull;
-    return;
-  }
-  if (need >= pairs - W) {
-    if (threadIdx.x == 0) thresh[bh] = ~0ull;
-    return;
-  }
+  const int64_t need = (budgets ? budgets[bh] : budget) - W;
+  TopupState s{0ull, need, 1, 0};
+  if (need <= 0) { s.mode = 0; thresh[bh] = 0ull; }
+  else if (need >= pairs - W) { s.mode = 2; thresh[bh] = ~0ull; }
+  st[bh] = s;
+}
+
+__global__ __launch_bounds__(256) void topup_hist_kernel(
+    const float* __restrict__ S, const uint32_t* __restrict__ bitmask, int nB, int words,
+    const TopupState* __restrict__ st, uint32_t* __restrict__ ghist, int pass) {
+  __shared__ uint32_t hist[256];
+  const int64_t bh = blockIdx.x;
+  const TopupState s = st[bh];
+  if (s.mode != 1) return;
+  for (int b = threadIdx.x; b < 256; b += 256) hist[b] = 0u;
+  __syncthreads();
+  const int64_t pairs = (int64_t)nB * nB;
+  const int64_t q0 = pairs * blockIdx.y / kSelSlices, q1 = pairs * (blockIdx.y + 1) / kSelSlices;
+  const int sh = pass == 7 ? 0 : 54 - 8 * pass;
+  const int hishift = pass == 0 ? 64 : sh + (pass == 7 ? 6 : 8);
+  const uint32_t dmask = pass == 7 ? 63u : 255u;
   const float* Sh = S + bh * pairs;
   const uint32_t* Bh = bitmask + bh * (int64_t)nB * words;
-  if (threadIdx.x == 0) { s_prefix = 0ull; s_need = need; }
-  __syncthreads();
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 54 - 8 * pass;       // digits at 54, 46, ..., 6, then 0 (6 bits)
-    const int sh = shift < 0 ? 0 : shift;
-    const int hishift = pass == 0 ? 64 : sh + (pass == 7 ? 6 : 8);
-    for (int b = threadIdx.x; b < 256; b += kSelThreads) hist[b] = 0u;
-    __syncthreads();
-    const uint64_t prefix = s_prefix;
-    for (int64_t q = threadIdx.x; q < pairs; q += kSelThreads) {
-      const int i = (int)(q / nB), j = (int)(q - (int64_t)i * nB);
-      if ((Bh[(int64_t)i * words + (j >> 5)] >> (j & 31)) & 1u) continue;
-      const uint64_t key = pair_key(Sh[q], i, j);
-      if (hishift < 64 && (key >> hishift) != prefix) continue;
-      const uint32_t digit = (uint32_t)((key >> sh) & (pass == 7 ? 63u : 255u));
-      atomicAdd(&hist[digit], 1u);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int64_t nd = s_need;
-      uint32_t d = 0;
-      for (; d < 256; ++d) {
-        if ((int64_t)hist[d] >= nd) break;
-        nd -= hist[d];
-      }
-      s_need = nd;
-      s_prefix = (prefix << (pass == 7 ? 6 : 8)) | d;
-    }
-    __syncthreads();
+  for (int64_t q = q0 + threadIdx.x; q < q1; q += 256) {
+    const int i = (int)(q / nB), j = (int)(q - (int64_t)i * nB);
+    if ((Bh[(int64_t)i * words + (j >> 5)] >> (j & 31)) & 1u) continue;
+    const uint64_t key = pair_key(Sh[q], i, j);
+    if (hishift < 64 && (key >> hishift) != s.prefix) continue;
+    atomicAdd(&hist[(uint32_t)(key >> sh) & dmask], 1u);
   }
-  if (threadIdx.x == 0) thresh[bh] = s_prefix + 1ull;
+  __syncthreads();
+  for (int b = threadIdx.x; b < 256; b += 256)
+    if (hist[b]) atomicAdd(&ghist[bh * 256 + b], hist[b]);
+}
+
+__global__ void topup_pick_kernel(TopupState* __restrict__ st, uint32_t* __restrict__ ghist,
+                                  uint64_t* __restrict__ thresh, int pass) {
+  const int bh = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  TopupState s = st[bh];
+  if (s.mode != 1) return;
+  uint32_t* h = ghist + bh * 256;
+  int64_t nd = s.need;
+  uint32_t d = 0;
+  for (; d < 256; ++d) {
+    if ((int64_t)h[d] >= nd) break;
+    nd -= h[d];
+  }
+  for (int b = 0; b < 256; ++b) h[b] = 0u;
+  s.need = nd;
+  s.prefix = (s.prefix << (pass == 7 ? 6 : 8)) | d;
+  st[bh] = s;
+  if (pass == 7) thresh[bh] = s.prefix + 1ull;
 }
 
 // One workgroup per row of a topped-up head: add pairs below the threshold,
@@ -520,9 +539,16 @@ void launch_topup_kernels(const Problem& p, const fva_mask& m, char* ws, int64_t
                           const int64_t* budgets, hipStream_t s) {
   const RouteWs L = route_ws_layout(p);
   uint64_t* thresh = (uint64_t*)(ws + L.thresh_off);
+  TopupState* st = (TopupState*)(ws + L.tstate_off);
+  uint32_t* ghist = (uint32_t*)(ws + L.thist_off);
   const int nheads = p.B * p.Hh;
-  hipLaunchKernelGGL(topup_select_kernel, dim3(nheads), dim3(kSelThreads), 0, s, m.scores,
-                     m.bitmask, m.head_count, p.nB, p.words, budget, budgets, thresh);
+  hipLaunchKernelGGL(topup_init_kernel, dim3(nheads), dim3(256), 0, s, m.head_count, p.nB,
+                     budget, budgets, nheads, st, ghist, thresh);
+  for (int pass = 0; pass < 8; ++pass) {
+    hipLaunchKernelGGL(topup_hist_kernel, dim3(nheads, kSelSlices), dim3(256), 0, s, m.scores,
+                       m.bitmask, p.nB, p.words, st, ghist, pass);
+    hipLaunchKernelGGL(topup_pick_kernel, dim3(nheads), dim3(64), 0, s, st, ghist, thresh, pass);
+  }
   hipLaunchKernelGGL(topup_apply_kernel, dim3((unsigned)p.rows), dim3(kRouteThreads), 0, s,
                      m.scores, p.nB, p.words, thresh, m.bitmask, m.row_count, m.col_idx,
                      m.head_count);

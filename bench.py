@@ -280,7 +280,30 @@ def main():
             "sparse_attn_ms": round(hev[2].elapsed_time(hev[3]), 4),
             "unreorder_ms": round(hev[3].elapsed_time(hev[4]), 4),
         }
-        # restore the raster-order state for what follows
+        # fixed Top-k control: every row keeps the Top-p run's mean row count,
+        # a uniform per-row load with the same executed work
+        kfix = int(round(nnz / (w.B * w.Hh * w.nB)))
+        prm_k = F.fva_route_params(0.0, kfix, 0, 0.0, 0)
+        for x, dst, lay in ((qd, buf.qr, F.FVA_LAYOUT_ROWS), (kd, buf.kr, F.FVA_LAYOUT_K64),
+                            (vd, buf.vt, F.FVA_LAYOUT_V64)):
+            F.fva_reorder(x, dst, w.B, w.Hh, w.d, g, F.token_strides(x), F.FVA_FORWARD, lay)
+        F.fva_route(buf.qr, buf.kr, w.B, w.Hh, w.d, g, prm_k, m, buf.route_ws,
+                    buf.sizes.route_ws_bytes, 0)
+        fk = {"topk": kfix}
+        for name, fl in (("static", F.FVA_SCHED_STATIC), ("queue", F.FVA_SCHED_QUEUE),
+                         ("xcd", F.FVA_SCHED_XCD)):
+            buf.trace.zero_()
+            k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            k0.record(stream)
+            F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, g, m, 0.0,
+                              fl | F.FVA_TRACE, buf.attn_ws, buf.sizes.attn_ws_bytes, buf.trace)
+            k1.record(stream)
+            torch.cuda.synchronize()
+            lc = lambda_cu(buf.trace.cpu().numpy().view(np.uint32), int(buf.sizes.rows))
+            fk[name] = {"lambda_cu": round(lc["lambda_cu"], 4),
+                        "attn_ms_traced": round(k0.elapsed_time(k1), 3)}
+        extras["fixed_topk_control"] = fk
+        # restore the raster-order Top-p state for what follows
         step(False)
         torch.cuda.synchronize()
 
