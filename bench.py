@@ -73,8 +73,14 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def lambda_cu(trace_u32, rows):
-    """Per-CU busy time (sum of item durations) -> max/mean over CUs."""
+def lambda_cu(trace_u32, rows, slots=512):
+    """Imbalance of one traced launch.
+
+    lambda_cu:   per-CU busy time (sum of its item durations), max/mean over CUs.
+    lambda_slot: critical path over mean slot load, span * slots / sum of item
+                 durations, with slots = resident workgroups (2 per CU here).  A
+                 CU hosting one long and one short workgroup looks balanced to
+                 lambda_cu but idles half its capacity; lambda_slot sees it."""
     import numpy as np
     tr = trace_u32.reshape(-1, 8)[:rows]
     t0 = tr[:, 4].astype(np.uint64) | (tr[:, 5].astype(np.uint64) << np.uint64(32))
@@ -86,7 +92,8 @@ def lambda_cu(trace_u32, rows):
     keys, inv = np.unique(cu_key, return_inverse=True)
     busy = np.bincount(inv, weights=dur)
     span = float(t1.max() - t0.min())
-    return dict(lambda_cu=float(busy.max() / busy.mean()), cus=int(len(keys)),
+    return dict(lambda_cu=float(busy.max() / busy.mean()),
+                lambda_slot=float(span * slots / dur.sum()), cus=int(len(keys)),
                 busy_max_ms=float(busy.max()) / 1e5, busy_mean_ms=float(busy.mean()) / 1e5,
                 span_ms=span / 1e5)
 
@@ -236,7 +243,9 @@ def main():
         extras["dense_ms"] = ms_dense
         extras["dense_tflops"] = de_flop / (ms_dense * 1e-3) / 1e12
         extras["speedup_vs_dense"] = ms_dense / ms_attn
-        # per-CU imbalance under the three schedules
+        # per-CU and per-slot imbalance under each schedule (2 resident
+        # workgroups per CU: 64 KB of LDS each)
+        slots = 2 * torch.cuda.get_device_properties(0).multi_processor_count
         lam = {}
         for name, fl in (("static", F.FVA_SCHED_STATIC), ("grid", F.FVA_SCHED_GRID),
                          ("queue", F.FVA_SCHED_QUEUE), ("xcd", F.FVA_SCHED_XCD)):
@@ -244,7 +253,8 @@ def main():
             F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, g, m, 0.0,
                               fl | F.FVA_TRACE, buf.attn_ws, buf.sizes.attn_ws_bytes, buf.trace)
             torch.cuda.synchronize()
-            lam[name] = lambda_cu(buf.trace.cpu().numpy().view(np.uint32), int(buf.sizes.rows))
+            lam[name] = lambda_cu(buf.trace.cpu().numpy().view(np.uint32), int(buf.sizes.rows),
+                                  slots)
         extras["lambda_cu"] = lam
 
     if not args.no_extras:
@@ -299,8 +309,9 @@ def main():
                               fl | F.FVA_TRACE, buf.attn_ws, buf.sizes.attn_ws_bytes, buf.trace)
             k1.record(stream)
             torch.cuda.synchronize()
-            lc = lambda_cu(buf.trace.cpu().numpy().view(np.uint32), int(buf.sizes.rows))
+            lc = lambda_cu(buf.trace.cpu().numpy().view(np.uint32), int(buf.sizes.rows), slots)
             fk[name] = {"lambda_cu": round(lc["lambda_cu"], 4),
+                        "lambda_slot": round(lc["lambda_slot"], 4),
                         "attn_ms_traced": round(k0.elapsed_time(k1), 3)}
         extras["fixed_topk_control"] = fk
         # restore the raster-order Top-p state for what follows
