@@ -430,13 +430,12 @@ __global__ void zero_counter(int32_t* ws) { ws[AttnWs::kQueueCtr] = 0; }
 // row lists out contiguously: XCD x owns [off[x], off[x+1]) and its heads
 // follow in assignment order, nB rows each.
 constexpr int kPlanThreads = 256;
-constexpr int kMaxHeads = 4096;
 
 __global__ __launch_bounds__(kPlanThreads) void xcd_assign_kernel(const int32_t* head_count,
                                                                   int nheads, int nB, int32_t* ws) {
-  __shared__ uint64_t keys[kMaxHeads];
-  __shared__ int16_t hx[kMaxHeads];
-  __shared__ int32_t hpos[kMaxHeads];
+  __shared__ uint64_t keys[kMaxXcdHeads];
+  __shared__ int16_t hx[kMaxXcdHeads];
+  __shared__ int32_t hpos[kMaxXcdHeads];
   int P = 1;
   while (P < nheads) P <<= 1;
   for (int h = threadIdx.x; h < P; h += kPlanThreads)
