@@ -454,3 +454,48 @@ def test_batch_of_two_full_path():
         attn(buf, fl)
         torch.cuda.synchronize()
         assert torch.equal(buf.orr.view(torch.int16), ref_rows.view(torch.int16))
+
+
+@pytest.mark.parametrize("slope", [12.0, -12.0, 40.0])
+def test_softmax_reference_moves_with_logit_ramps(slope):
+    # Logits change by `slope` nats per 64-key sub-tile along the reordered key
+    # axis (about 280 log2 units end to end at |slope| = 12), so with a rising
+    # ramp the running reference max of the online softmax has to move on every
+    # sub-tile, far past what exp2 could hold without rescaling; a falling ramp
+    # keeps the first reference.  All blocks are selected (p = 1).
+    w = small_workload("ramp", 2, 128, (2, 16, 32), (1, 8, 16), 1.0, 0)
+    N = w.N
+    order = O.block_order(*w.grid, *w.block)     # reordered position -> token
+    pos = np.empty(N, dtype=np.float64)
+    pos[order] = np.arange(N)
+    a = 8.0
+    kval = slope * (pos / 64.0) / (a * w.scale)
+    g = torch.Generator().manual_seed(7)
+    q = torch.zeros(1, N, w.Hh, w.d)
+    k = torch.zeros(1, N, w.Hh, w.d)
+    q[:, :, :, 0] = a
+    k[:, :, :, 0] = torch.from_numpy(kval).float()[None, :, None]
+    q[:, :, :, 1:] = 0.05 * torch.randn(1, N, w.Hh, w.d - 1, generator=g)
+    k[:, :, :, 1:] = 0.05 * torch.randn(1, N, w.Hh, w.d - 1, generator=g)
+    v = torch.randn(1, N, w.Hh, w.d, generator=g)
+    q, k, v = q.bfloat16(), k.bfloat16(), v.bfloat16()
+    buf = F.alloc_buffers(w.grid, w.block, w.B, w.Hh, w.d, trace=True)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    gpu_reorder(buf, qd, kd, vd)
+    route(buf, w, top_p=1.0, topk=0, aug=0)
+    full = np.ones((w.B, w.Hh, w.nB, w.nB), dtype=bool)
+    ref = _oracle_attention(w, q, k, v, full)
+    for fl in (F.FVA_SCHED_QUEUE, F.FVA_SCHED_XCD):
+        buf.orr.fill_(float("nan"))
+        attn(buf, fl)
+        torch.cuda.synchronize()
+        got = to_np(buf.orr)
+        assert np.isfinite(got).all()
+        mx, rel = err_stats(got[:, :, :N], ref[:, :, :N])
+        print(f"slope {slope}: max_abs={mx:.3e} mean_rel={rel:.3e}")
+        assert mx <= MAX_ABS and rel <= MEAN_REL
+    # the dense comparator takes the same path
+    F.fva_dense_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, buf.grid)
+    torch.cuda.synchronize()
+    mx, rel = err_stats(to_np(buf.orr)[:, :, :N], ref[:, :, :N])
+    assert mx <= MAX_ABS and rel <= MEAN_REL
