@@ -206,6 +206,56 @@ __device__ void bitonic_sort(K* keys, int P) {
   }
 }
 
+// Ascending bitonic sort of P = 256*E 64-bit keys, E per thread in
+// registers: thread t holds positions t*E .. t*E+E-1, before and after.  A
+// compare-exchange partner closer than E is in the same thread, one closer
+// than 64*E is in the same wave (lane exchange), and only farther partners go
+// through LDS, with a barrier.
+template <int E>
+__device__ void bitonic_sort_regs(uint64_t (&v)[E], uint64_t* xch) {
+  constexpr int P = 256 * E;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int k = 2; k <= P; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j < E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if (e & j) continue;
+          const bool up = ((t * E + e) & k) == 0;
+          const uint64_t x = v[e], y = v[e | j];
+          if ((x > y) == up) { v[e] = y; v[e | j] = x; }
+        }
+      } else {
+        uint64_t o[E];
+        if (j < 64 * E) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v[e], j / E, 64);
+            const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v[e] >> 32), j / E, 64);
+            o[e] = ((uint64_t)hi << 32) | lo;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) xch[t * E + e] = v[e];
+          __syncthreads();
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[e] = xch[(t * E + e) ^ j];
+          __syncthreads();
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = t * E + e;
+          const bool keep_min = ((i & j) == 0) == ((i & k) == 0);
+          const bool less = v[e] < o[e];
+          v[e] = (keep_min == less) ? v[e] : o[e];
+        }
+      }
+    }
+  }
+}
+
 // Writes bitmask words, and the ascending column list, of one row from the
 // LDS bitmask `bits` (words entries).  Returns nothing; col_idx gets popcount
 // entries.  Must be called by all threads of the block.
@@ -235,51 +285,56 @@ __device__ void emit_row(const uint32_t* bits, int words, uint32_t* bm_out, int1
 constexpr int kRouteThreads = 256;
 constexpr int kMaxNB = 2048;
 
+template <int E>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
-    const float* __restrict__ S, int nB, int words, int P, float top_p, int topk,
+    const float* __restrict__ S, int nB, int words, float top_p, int topk,
     uint32_t* __restrict__ bitmask, int32_t* __restrict__ row_count,
     int16_t* __restrict__ col_idx, int32_t* __restrict__ head_count, uint32_t* flags) {
-  __shared__ uint64_t keys[kMaxNB];
+  __shared__ uint64_t xch[256 * E];
   __shared__ uint32_t bits[kMaxNB / 32];
   __shared__ double wsum[4];
   __shared__ int red[4];
   __shared__ int wpre[kMaxNB / 32];
+  __shared__ double s_max;
   const int64_t row = blockIdx.x;
   const int64_t bh = row / nB;
   const float* s = S + row * nB;
+  const int t0 = threadIdx.x * E;  // this thread's sort positions t0 .. t0+E-1
   int nan_seen = 0;
-  for (int j = threadIdx.x; j < P; j += kRouteThreads) {
+  uint64_t v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = t0 + e;
     uint64_t key = ~0ull;
     if (j < nB) {
-      const float v = s[j];
-      nan_seen |= (v != v);
-      key = ((uint64_t)(~order_key(v)) << 32) | (uint32_t)j;
+      const float x = s[j];
+      nan_seen |= (x != x);
+      key = ((uint64_t)(~order_key(x)) << 32) | (uint32_t)j;
     }
-    keys[j] = key;
+    v[e] = key;
   }
   for (int w = threadIdx.x; w < words; w += kRouteThreads) bits[w] = 0u;
   if (nan_seen) atomicOr(flags, 1u);
+  bitonic_sort_regs<E>(v, xch);
+  if (threadIdx.x == 0) s_max = (double)order_key_inv(~(uint32_t)(v[0] >> 32));
   __syncthreads();
-  bitonic_sort<uint64_t, kRouteThreads>(keys, P);
 
   // float64 softmax mass accumulated in importance order
-  const int ept = P / kRouteThreads;           // consecutive sorted slots per thread
-  const int t0 = threadIdx.x * ept;
   int nstar;
   if (top_p >= 1.0f) {
     nstar = nB;
   } else if (top_p <= 0.0f) {
     nstar = 0;
   } else {
-    const double m = (double)order_key_inv(~(uint32_t)(keys[0] >> 32));
-    double e[8];
+    const double m = s_max;
+    double ev[E];
     double local = 0.0;
-    for (int u = 0; u < ept; ++u) {
-      const int t = t0 + u;
-      double v = 0.0;
-      if (t < nB) v = exp((double)order_key_inv(~(uint32_t)(keys[t] >> 32)) - m);
-      e[u] = v;
-      local += v;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      double x = 0.0;
+      if (t0 + e < nB) x = exp((double)order_key_inv(~(uint32_t)(v[e] >> 32)) - m);
+      ev[e] = x;
+      local += x;
     }
     const double incl = block_incl_scan_f64(local, wsum);
     __shared__ double Zs;
@@ -288,17 +343,18 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const double target = (double)top_p * Zs;
     double c = incl - local;
     int below = 0;
-    for (int u = 0; u < ept; ++u) {
-      c += e[u];
-      if (t0 + u < nB && c < target) ++below;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      c += ev[e];
+      if (t0 + e < nB && c < target) ++below;
     }
     nstar = min(nB, block_sum_i32<kRouteThreads>(below, red) + 1);
   }
   const int n = min(nB, max(nstar, topk));
-  for (int u = 0; u < ept; ++u) {
-    const int t = t0 + u;
-    if (t < n) {
-      const uint32_t j = (uint32_t)keys[t];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (t0 + e < n) {
+      const uint32_t j = (uint32_t)v[e];
       atomicOr(&bits[j >> 5], 1u << (j & 31));
     }
   }
@@ -595,11 +651,16 @@ fva_status launch_route(const Problem& p, const void* qr, const void* kr,
       hipLaunchKernelGGL(score_kernel<64>, sg, dim3(256), 0, s, qbar, kbar, m.scores, p.nB,
                          scale);
   }
-  int P = 256;
-  while (P < p.nB) P <<= 1;
-  hipLaunchKernelGGL(route_kernel, dim3((unsigned)p.rows), dim3(kRouteThreads), 0, s, m.scores,
-                     p.nB, p.words, P, prm.top_p, prm.topk_floor, m.bitmask, m.row_count,
-                     m.col_idx, m.head_count, wflags);
+  // sort length: the power of two >= nB, at least one key per thread
+#define FVA_ROUTE(E)                                                                         \
+  hipLaunchKernelGGL(route_kernel<E>, dim3((unsigned)p.rows), dim3(kRouteThreads), 0, s, m.scores, \
+                     p.nB, p.words, prm.top_p, prm.topk_floor, m.bitmask, m.row_count,        \
+                     m.col_idx, m.head_count, wflags)
+  if (p.nB <= 256) FVA_ROUTE(1);
+  else if (p.nB <= 512) FVA_ROUTE(2);
+  else if (p.nB <= 1024) FVA_ROUTE(4);
+  else FVA_ROUTE(8);
+#undef FVA_ROUTE
   if (prm.aug_budget > 0) launch_topup_kernels(p, m, ws, (int64_t)prm.aug_budget, nullptr, s);
   launch_queue(p, m, ws, s);
   return hip_fail(hipGetLastError(), "route launch");
