@@ -142,7 +142,7 @@ def cpu_baseline(w, q, k, v, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the path runs on one GPU (its per-GPU share of heads); --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import numpy as np
