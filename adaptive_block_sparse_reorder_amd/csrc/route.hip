@@ -31,10 +31,11 @@ __global__ void zero_route_state(int32_t* head_count, int nheads, uint32_t* flag
 }
 
 // ------------------------------------------------------------------ pooling
-// grid (nB, B*Hh, 2 [q|k]); 256 threads.  Q is in the rows layout: thread =
-// (row group, 16-byte chunk).  K is in the k64 tile layout: wave w owns the
-// 16-byte channel chunks c = w + 4k and lane r token r of each 64-token tile,
-// then the 64 lanes are reduced with shuffles.
+// grid (nB, B*Hh, 2 [q|k]); 256 threads.  Thread = (row group, 16-byte channel
+// chunk) for both Q (rows layout) and K (k64 tile layout, where a wave's four
+// row groups read four consecutive 16-byte units of each chunk); the row
+// groups of a wave are reduced with two (d=128) or three (d=64) shuffles, the
+// four waves through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ qr,
                                                    const uint16_t* __restrict__ kr,
@@ -48,69 +49,37 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
   const int64_t bh = blockIdx.y;
   const int nreal = (int)min((int64_t)BLK, N - (int64_t)blk * BLK);
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  if (blockIdx.z == 0) {
-    const uint16_t* x = qr + (bh * Npad + (int64_t)blk * BLK) * D;
-    const int c = threadIdx.x % CPR;
-    const int rg = threadIdx.x / CPR;
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int r = rg; r < nreal; r += RG) {
-      const u32x4 v = *(const u32x4*)(x + (int64_t)r * D + c * 8);
-      acc[0] += bf16_lo(v.x); acc[1] += bf16_hi(v.x);
-      acc[2] += bf16_lo(v.y); acc[3] += bf16_hi(v.y);
-      acc[4] += bf16_lo(v.z); acc[5] += bf16_hi(v.z);
-      acc[6] += bf16_lo(v.w); acc[7] += bf16_hi(v.w);
-    }
-    // reduce the row groups of this wave (lanes that share a chunk)
+  // thread -> 16-byte chunk c of rows rg, rg+RG, ...; Q rows are token-major,
+  // K is in k64 tiles (unit (c, r) of a 64-token tile at (c*64 + r)*16 bytes)
+  const bool is_k = blockIdx.z != 0;
+  const uint16_t* x = (is_k ? kr : qr) + (bh * Npad + (int64_t)blk * BLK) * D;
+  const int c = threadIdx.x % CPR;
+  const int rg = threadIdx.x / CPR;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r = rg; r < nreal; r += RG) {
+    const int64_t unit = is_k ? (int64_t)(r >> 6) * 64 * CPR + c * 64 + (r & 63)
+                              : (int64_t)r * CPR + c;
+    const u32x4 v = *(const u32x4*)(x + unit * 8);
+    acc[0] += bf16_lo(v.x); acc[1] += bf16_hi(v.x);
+    acc[2] += bf16_lo(v.y); acc[3] += bf16_hi(v.y);
+    acc[4] += bf16_lo(v.z); acc[5] += bf16_hi(v.z);
+    acc[6] += bf16_lo(v.w); acc[7] += bf16_hi(v.w);
+  }
+  // reduce the row groups of this wave (lanes that share a chunk), then across waves
 #pragma unroll
-    for (int off = CPR; off < 64; off <<= 1) {
+  for (int off = CPR; off < 64; off <<= 1) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
-    }
-    if (lane < CPR) {
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
+  }
+  if (lane < CPR) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) part[wave][c * 8 + e] = acc[e];
-    }
-    __syncthreads();
-    if (threadIdx.x < D) {
-      const float sum = (part[0][threadIdx.x] + part[1][threadIdx.x]) +
-                        (part[2][threadIdx.x] + part[3][threadIdx.x]);
-      qbar[(bh * nB + blk) * D + threadIdx.x] = sum / (float)nreal;
-    }
-  } else {
-    constexpr int CW = CPR / 4;  // chunks per wave
-    const uint16_t* x = kr + (bh * Npad + (int64_t)blk * BLK) * D;  // first tile of the block
-    float acc[CW][8];
-#pragma unroll
-    for (int k = 0; k < CW; ++k)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
-    for (int t0 = 0; t0 < nreal; t0 += 64) {
-      if (t0 + lane < nreal) {
-        const uint16_t* tile = x + (int64_t)t0 * D;
-#pragma unroll
-        for (int k = 0; k < CW; ++k) {
-          const int c = wave + 4 * k;
-          const u32x4 v = *(const u32x4*)(tile + (c * 64 + lane) * 8);
-          acc[k][0] += bf16_lo(v.x); acc[k][1] += bf16_hi(v.x);
-          acc[k][2] += bf16_lo(v.y); acc[k][3] += bf16_hi(v.y);
-          acc[k][4] += bf16_lo(v.z); acc[k][5] += bf16_hi(v.z);
-          acc[k][6] += bf16_lo(v.w); acc[k][7] += bf16_hi(v.w);
-        }
-      }
-    }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1)
-#pragma unroll
-      for (int k = 0; k < CW; ++k)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[k][e] += __shfl_xor(acc[k][e], off, 64);
-    if (lane == 0) {
-      float* out = kbar + (bh * nB + blk) * D;
-#pragma unroll
-      for (int k = 0; k < CW; ++k)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) out[(wave + 4 * k) * 8 + e] = acc[k][e] / (float)nreal;
-    }
+    for (int e = 0; e < 8; ++e) part[wave][c * 8 + e] = acc[e];
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const float sum = (part[0][threadIdx.x] + part[1][threadIdx.x]) +
+                      (part[2][threadIdx.x] + part[3][threadIdx.x]);
+    (is_k ? kbar : qbar)[(bh * nB + blk) * D + threadIdx.x] = sum / (float)nreal;
   }
 }
 
