@@ -56,9 +56,21 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ void g2lds16(const void* g, char* lds_uniform) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_uniform, 16, 0,
-                                   0);
+// Raw byte buffer over [base, base + bytes): the resource lives in SGPRs, so a
+// copy needs only a 32-bit per-lane offset (data format 32, as gfx9 raw
+// buffers use; accesses past `bytes` read zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_buffer(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// 16 bytes per lane from buffer rs at voff + soff (soff wave-uniform) into LDS
+// at lds_uniform + 16*lane.  HBM->LDS copies issued as buffer loads leave the
+// matrix cores' issue rate nearly untouched; the same copies with a 64-bit
+// per-lane address cost a sixth of it when one is issued per four MFMAs.
+__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                                          char* lds_uniform) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rs, (__attribute__((address_space(3))) void*)lds_uniform, 16, voff, soff, 0, 0);
 }
 
 // LDS tiles are verbatim copies of the k64 / v64 HBM tiles:
@@ -204,22 +216,23 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_
     }
     U = __builtin_amdgcn_readfirstlane(U);
 
-    const uint16_t* kbase = a.kr + bh * a.Npad * D;
-    const uint16_t* vbase = a.vt + bh * a.Npad * D;  // tiles of key0 start at key0*D
+    // this head's K and V tiles (the tile of key0 starts at element key0*D)
+    const __amdgpu_buffer_rsrc_t kbuf = byte_buffer(a.kr + bh * a.Npad * D, (int)(a.Npad * D * 2));
+    const __amdgpu_buffer_rsrc_t vbuf = byte_buffer(a.vt + bh * a.Npad * D, (int)(a.Npad * D * 2));
 
     auto key0_of = [&](int u) -> int64_t {
       const int t = u / NSUB, half = u % NSUB;
       const int kb = DENSE ? t : __builtin_amdgcn_readfirstlane((int)s_cols[t]);
       return (int64_t)kb * BLK + half * KT;
     };
-    auto load_tile = [&](const uint16_t* base, int u, char* buf) {
-      const char* src = (const char*)(base + key0_of(u) * D) + loff;
+    auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, int u, char* buf) {
+      const uint32_t soff = (uint32_t)(key0_of(u) * D * 2);
 #pragma unroll
       for (int k = 0; k < LOADS; ++k)
-        g2lds16(src + k * NW * 1024, buf + (k * NW + wave) * 1024);
+        buf2lds16(rs, loff, soff + k * NW * 1024, buf + (k * NW + wave) * 1024);
     };
-    auto load_k = [&](int u) { load_tile(kbase, u, lds + (u & 1) * TILE); };
-    auto load_v = [&](int u) { load_tile(vbase, u, lds + (2 + (u & 1)) * TILE); };
+    auto load_k = [&](int u) { load_tile(kbuf, u, lds + (u & 1) * TILE); };
+    auto load_v = [&](int u) { load_tile(vbuf, u, lds + (2 + (u & 1)) * TILE); };
 
     // Q^T operands: q-tile j of this wave = 32 queries; lane holds query l32, d chunk 2kk+hl
     const int64_t q0 = (int64_t)qb * BLK + wave * 32 * QT;
