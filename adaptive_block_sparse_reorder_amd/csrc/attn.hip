@@ -5,10 +5,10 @@
 // Work item = one query block (BLK rows) of one head, processed by one
 // workgroup of BLK/32 waves; each wave owns 32 queries and walks every
 // selected key block of the row in 64-key sub-tiles.  A sub-tile of K and V
-// (32 KB at d=128) is staged in LDS by direct HBM->LDS loads
-// (global_load_lds_dwordx4), double-buffered, so a workgroup uses 64 KB and
-// two independent workgroups share a CU: while one is in its softmax the
-// other keeps the matrix cores busy.
+// (32 KB at d=128) is staged in LDS by direct HBM->LDS buffer loads
+// (buffer_load_dwordx4 with the LDS destination), double-buffered, so a
+// workgroup uses 64 KB and two independent workgroups share a CU: while one
+// is in its softmax the other keeps the matrix cores busy.
 //
 // Products use v_mfma_f32_32x32x16_bf16 in transposed form:
 //   S^T (keys x queries) = K * Q^T     A = K from LDS, B = Q^T in registers
