@@ -139,6 +139,32 @@ def cpu_baseline(w, q, k, v, seconds):
     }
 
 
+def gemm_reference(attn_tflops, n=8192, reps=50):
+    """Practical bf16 MFMA rate of this card: the vendor GEMM (torch.matmul)
+    on random normal operands.  Data-dependent power, not the issue rate, sets
+    the clock it runs at, so it is the reference the attention kernel's rate is
+    read against (the published peak stays the roofline's peak)."""
+    import torch
+
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=gen)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=gen)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    tf = 2.0 * n ** 3 / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12
+    del a, b, c
+    return {"library": "torch.matmul (hipBLASLt), random normal bf16 operands", "n": n,
+            "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "attn_over_gemm": round(attn_tflops / tf, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -243,6 +269,7 @@ def main():
         extras["dense_ms"] = ms_dense
         extras["dense_tflops"] = de_flop / (ms_dense * 1e-3) / 1e12
         extras["speedup_vs_dense"] = ms_dense / ms_attn
+        extras["gemm_reference"] = gemm_reference(attn_tflops)
         # per-CU and per-slot imbalance under each schedule (2 resident
         # workgroups per CU: 64 KB of LDS each)
         slots = 2 * torch.cuda.get_device_properties(0).multi_processor_count
