@@ -106,6 +106,7 @@ struct AttnArgs {
   const int32_t* queue;    // heaviest-first queue, or the XCD-ordered list
   int32_t* ws;             // attention workspace (int view)
   uint32_t* trace;
+  float* lse;              // optional: per-query log-sum-exp, [B*Hh, N]
   int64_t N, Npad;
   int64_t rows;
   int nB;
@@ -401,6 +402,10 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_
       const float inv = l > 0.f ? 1.f / l : 0.f;
       const int64_t q = q0 + 32 * j + l32;
       const float sc_ = q < a.N ? inv : 0.f;
+      // natural log-sum-exp of the scaled scores over the keys used:
+      // sum_k exp2(s_k * sl2) = 2^m_use * l
+      if (a.lse && hl == 0 && q < a.N)
+        a.lse[bh * a.N + q] = l > 0.f ? (m_use[j] + log2f(l)) * 0.69314718055994531f : -INFINITY;
       uint16_t* op = a.out + (bh * a.Npad + q) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -555,7 +560,7 @@ size_t attn_ws_bytes(const Problem& p) { return AttnWs::bytes((int64_t)p.B * p.H
 
 fva_status launch_attn(const Problem& p, const void* qr, const void* kr, const void* vt,
                        void* out, const fva_mask* m, float scale, int flags, void* ws,
-                       void* trace, bool dense, hipStream_t s) {
+                       void* trace, void* lse, bool dense, hipStream_t s) {
   AttnArgs a;
   a.qr = (const uint16_t*)qr;
   a.kr = (const uint16_t*)kr;
@@ -567,6 +572,7 @@ fva_status launch_attn(const Problem& p, const void* qr, const void* kr, const v
   a.queue = m ? m->queue : nullptr;
   a.ws = (int32_t*)ws;
   a.trace = (uint32_t*)trace;
+  a.lse = (float*)lse;
   a.N = p.N;
   a.Npad = p.Npad;
   a.rows = p.rows;

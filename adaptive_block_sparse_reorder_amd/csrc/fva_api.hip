@@ -251,7 +251,7 @@ static fva_status attn_common(const void* qr, const void* kr, const void* vt, vo
 fva_status fva_sparse_attn(const void* qr, const void* kr, const void* vt, void* out, int32_t B,
                            int32_t Hh, int32_t d, const fva_grid* grid, const fva_mask* mask,
                            float scale, int32_t flags, void* ws, size_t ws_bytes, void* trace,
-                           hipStream_t stream) {
+                           void* lse, hipStream_t stream) {
   Problem p;
   fva_status st = attn_common(qr, kr, vt, out, B, Hh, d, grid, &p);
   if (st != FVA_OK) return st;
@@ -268,19 +268,21 @@ fva_status fva_sparse_attn(const void* qr, const void* kr, const void* vt, void*
   if (((uintptr_t)ws & 255u) != 0) return fail(FVA_ERR_WORKSPACE, "workspace not 256-byte aligned");
   if ((flags & FVA_TRACE) && !trace) return fail(FVA_ERR_INVALID_ARG, "FVA_TRACE needs a trace buffer");
   if (!(flags & FVA_TRACE)) trace = nullptr;
+  if (((uintptr_t)lse & 3u) != 0) return fail(FVA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
   if (!(scale > 0.f)) scale = 1.0f / sqrtf((float)d);
-  return launch_attn(p, qr, kr, vt, out, mask, scale, flags, ws, trace, false, stream);
+  return launch_attn(p, qr, kr, vt, out, mask, scale, flags, ws, trace, lse, false, stream);
 }
 
 fva_status fva_dense_attn(const void* qr, const void* kr, const void* vt, void* out, int32_t B,
                           int32_t Hh, int32_t d, const fva_grid* grid, float scale,
-                          hipStream_t stream) {
+                          void* lse, hipStream_t stream) {
   Problem p;
   fva_status st = attn_common(qr, kr, vt, out, B, Hh, d, grid, &p);
   if (st != FVA_OK) return st;
+  if (((uintptr_t)lse & 3u) != 0) return fail(FVA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
   if (!(scale > 0.f)) scale = 1.0f / sqrtf((float)d);
-  return launch_attn(p, qr, kr, vt, out, nullptr, scale, FVA_SCHED_GRID, nullptr, nullptr, true,
-                     stream);
+  return launch_attn(p, qr, kr, vt, out, nullptr, scale, FVA_SCHED_GRID, nullptr, nullptr, lse,
+                     true, stream);
 }
 
 const char* fva_status_string(fva_status s) {

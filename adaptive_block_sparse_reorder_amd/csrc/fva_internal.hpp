@@ -57,7 +57,7 @@ fva_status launch_topup(const Problem& p, const int64_t* budgets, const fva_mask
                         hipStream_t s);
 fva_status launch_attn(const Problem& p, const void* qr, const void* kr, const void* vt,
                        void* out, const fva_mask* m, float scale, int flags, void* ws,
-                       void* trace, bool dense, hipStream_t s);
+                       void* trace, void* lse, bool dense, hipStream_t s);
 
 // ---------------------------------------------------------------- device side
 

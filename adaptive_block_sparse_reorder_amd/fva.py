@@ -101,8 +101,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                               I32, P]
     lib.fva_route_flags.argtypes = [P, ctypes.POINTER(ctypes.c_uint32), P]
     lib.fva_sparse_attn.argtypes = [P, P, P, P, I32, I32, I32, ctypes.POINTER(fva_grid),
-                                    ctypes.POINTER(fva_mask), F, I32, P, SZ, P, P]
-    lib.fva_dense_attn.argtypes = [P, P, P, P, I32, I32, I32, ctypes.POINTER(fva_grid), F, P]
+                                    ctypes.POINTER(fva_mask), F, I32, P, SZ, P, P, P]
+    lib.fva_dense_attn.argtypes = [P, P, P, P, I32, I32, I32, ctypes.POINTER(fva_grid), F, P, P]
     lib.fva_reorder_ex.argtypes = [P, P, I32, I32, I32, ctypes.POINTER(fva_grid), P,
                                    ctypes.POINTER(ctypes.c_int64), I32, I32, P]
     lib.fva_tile_order_bytes.argtypes = [ctypes.POINTER(fva_grid), ctypes.POINTER(ctypes.c_size_t)]
@@ -221,18 +221,22 @@ def fva_route_flags(ws, stream=None) -> int:
 
 def fva_sparse_attn(qr, kr, vt, out, B: int, Hh: int, d: int, grid: fva_grid, mask: fva_mask,
                     scale: float = 0.0, flags: int = FVA_SCHED_QUEUE, ws=None, ws_bytes: int = 0,
-                    trace=None, stream=None):
+                    trace=None, stream=None, lse=None):
+    """lse: optional float32 device tensor of B*Hh*N entries (per-query
+    log-sum-exp of the scaled scores over the keys used)."""
     lib = load_library()
     _check(lib.fva_sparse_attn(_ptr(qr), _ptr(kr), _ptr(vt), _ptr(out), B, Hh, d,
                                ctypes.byref(grid), ctypes.byref(mask), scale, flags, _ptr(ws),
-                               ws_bytes, _ptr(trace), _stream(stream)), "fva_sparse_attn")
+                               ws_bytes, _ptr(trace), _ptr(lse), _stream(stream)),
+           "fva_sparse_attn")
 
 
 def fva_dense_attn(qr, kr, vt, out, B: int, Hh: int, d: int, grid: fva_grid, scale: float = 0.0,
-                   stream=None):
+                   stream=None, lse=None):
     lib = load_library()
     _check(lib.fva_dense_attn(_ptr(qr), _ptr(kr), _ptr(vt), _ptr(out), B, Hh, d,
-                              ctypes.byref(grid), scale, _stream(stream)), "fva_dense_attn")
+                              ctypes.byref(grid), scale, _ptr(lse), _stream(stream)),
+           "fva_dense_attn")
 
 
 def fva_rlb_plan(head_count, ranks: int, topology: int = FVA_RLB_PAIRS):

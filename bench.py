@@ -139,6 +139,17 @@ def cpu_baseline(w, q, k, v, seconds):
     }
 
 
+def recall_stats(lse_sel, lse_all):
+    """Share of each query's full softmax mass held by its selected blocks,
+    exp(lse_sel - lse_all), over every real query of every head."""
+    import torch
+
+    r = torch.exp(lse_sel.double() - lse_all.double())
+    return {"mean": round(float(r.mean()), 5),
+            "p05": round(float(torch.quantile(r.float(), 0.05)), 5),
+            "min": round(float(r.min()), 5)}
+
+
 def gemm_reference(attn_tflops, n=8192, reps=50):
     """Practical bf16 MFMA rate of this card: the vendor GEMM (torch.matmul)
     on random normal operands.  Data-dependent power, not the issue rate, sets
@@ -270,6 +281,16 @@ def main():
         extras["dense_tflops"] = de_flop / (ms_dense * 1e-3) / 1e12
         extras["speedup_vs_dense"] = ms_dense / ms_attn
         extras["gemm_reference"] = gemm_reference(attn_tflops)
+        # mask recall: per-query log-sum-exp of the sparse and the dense kernel
+        nq = w.B * w.Hh * w.N
+        lse_all = torch.empty(nq, dtype=torch.float32, device="cuda")
+        lse_sel = torch.empty(nq, dtype=torch.float32, device="cuda")
+        F.fva_dense_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, g, lse=lse_all)
+        F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, g, m, 0.0, args.sched,
+                          buf.attn_ws, buf.sizes.attn_ws_bytes, None, lse=lse_sel)
+        torch.cuda.synchronize()
+        recall = {"definition": "exp(lse_sparse - lse_dense) per real query, all heads",
+                  "topp_raster": recall_stats(lse_sel, lse_all)}
         # per-CU and per-slot imbalance under each schedule (2 resident
         # workgroups per CU: 64 KB of LDS each)
         slots = 2 * torch.cuda.get_device_properties(0).multi_processor_count
@@ -309,6 +330,13 @@ def main():
         hev[4].record(stream)
         torch.cuda.synchronize()
         hnnz = int(buf.row_count.sum().item())
+        lse_hall = torch.empty(nq, dtype=torch.float32, device="cuda")
+        F.fva_dense_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, g, lse=lse_hall)
+        F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, g, m, 0.0, args.sched,
+                          buf.attn_ws, buf.sizes.attn_ws_bytes, None, lse=lse_sel)
+        torch.cuda.synchronize()
+        recall["topp_hilbert"] = recall_stats(lse_sel, lse_hall)
+        del lse_hall
         extras["hilbert_order"] = {
             "density_mean": round(hnnz / (w.B * w.Hh * w.nB ** 2), 4),
             "density_mean_raster": round(nnz / (w.B * w.Hh * w.nB ** 2), 4),
@@ -340,6 +368,10 @@ def main():
             fk[name] = {"lambda_cu": round(lc["lambda_cu"], 4),
                         "lambda_slot": round(lc["lambda_slot"], 4),
                         "attn_ms_traced": round(k0.elapsed_time(k1), 3)}
+        F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, g, m, 0.0, args.sched,
+                          buf.attn_ws, buf.sizes.attn_ws_bytes, None, lse=lse_sel)
+        torch.cuda.synchronize()
+        recall["topk_fixed_raster"] = recall_stats(lse_sel, lse_all)
         extras["fixed_topk_control"] = fk
         # restore the raster-order Top-p state for what follows
         step(False)
@@ -364,6 +396,12 @@ def main():
     F.fva_topup(w.B, w.Hh, w.d, g, dev_budgets, m, buf.route_ws, buf.sizes.route_ws_bytes)
     e1.record(stream)
     torch.cuda.synchronize()
+    if not args.no_extras:
+        F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, g, m, 0.0, args.sched,
+                          buf.attn_ws, buf.sizes.attn_ws_bytes, None, lse=lse_sel)
+        torch.cuda.synchronize()
+        recall["topp_raster_after_sasa"] = recall_stats(lse_sel, lse_all)
+        extras["mask_recall"] = recall
     extras["sasa_alpha_0.5"] = {
         "topup_ms": round(e0.elapsed_time(e1), 4),
         "pairs_added": int(sum(budgets) - sum(hc)),

@@ -216,17 +216,27 @@ fva_status fva_route_flags(const void* ws, uint32_t* flags_out, hipStream_t stre
  * (scheduler counters and lists; contents need not be initialized).
  * trace (with FVA_TRACE): trace_bytes bytes; record k (8 x uint32) describes
  * the k-th processed queue entry: {row, XCC_ID, HW_ID, workgroup id,
- * t0 lo, t0 hi, t1 lo, t1 hi} with t = s_memrealtime ticks (100 MHz).     */
+ * t0 lo, t0 hi, t1 lo, t1 hi} with t = s_memrealtime ticks (100 MHz).
+ * lse (optional, NULL to skip): float32 [B*Hh, N], 4-byte aligned, indexed
+ * by reordered query position; entry i is the natural log-sum-exp of the
+ * scaled scores over the keys that query used,
+ *   lse_i = log sum_k exp((q_i . k) * scale)   (-inf with no selected block).
+ * Against the dense kernel's lse, exp(lse_sparse - lse_dense) is the share of
+ * the query's full softmax mass that the selected blocks hold (the recall of
+ * the mask; block-sparse quality is framed this way on the DFSAttn abstract
+ * listed at thelatestinai.com/papers/2607.16190).                          */
 fva_status fva_sparse_attn(const void* qr, const void* kr, const void* vt, void* out,
                            int32_t B, int32_t Hh, int32_t d, const fva_grid* grid,
                            const fva_mask* mask, float scale, int32_t flags,
-                           void* ws, size_t ws_bytes, void* trace, hipStream_t stream);
+                           void* ws, size_t ws_bytes, void* trace, void* lse,
+                           hipStream_t stream);
 
 /* Dense attention over every key block with the same core: the comparator
- * for the sparse kernel.  Same layouts and output convention as above.     */
+ * for the sparse kernel.  Same layouts, output and lse conventions as above
+ * (lse then sums over all real keys).                                      */
 fva_status fva_dense_attn(const void* qr, const void* kr, const void* vt, void* out,
                           int32_t B, int32_t Hh, int32_t d, const fva_grid* grid,
-                          float scale, hipStream_t stream);
+                          float scale, void* lse, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Load balancing and slack-aware augmentation on virtual ranks (FVAttn

@@ -33,6 +33,12 @@ Steps and the passages they follow (all on the FVAttn page):
                                      workloads), one-GPU work-queue form
   sparse_attention                   section 2 (only selected query-key block pairs
                                      are evaluated)
+  sparse_lse / mask_recall           section 2 (the softmax normalizer over the keys
+                                     of the selected blocks); recall as the share of
+                                     the full softmax mass those keys hold (reading;
+                                     block-sparse quality is framed as attention
+                                     recall on the DFSAttn abstract listed at
+                                     thelatestinai.com/papers/2607.16190)
 
 Every function here is pinned by tests against closed forms, brute force on
 tiny inputs, or a library routine for a special case (dense attention).
@@ -454,6 +460,47 @@ def sparse_attention(qr, kr, vr, mask, N: int, BLK: int, scale: float,
         res[(b, h, i)] = sparse_attention_block(qr[b, h], kr[b, h], vr[b, h],
                                                 mask[b, h, i], N, BLK, scale, i)
     return res
+
+
+def _selected_keys(mask_row, N: int, BLK: int) -> np.ndarray:
+    sel = np.nonzero(mask_row)[0]
+    if sel.size == 0:
+        return np.zeros(0, dtype=np.int64)
+    return np.concatenate([np.arange(j * BLK, min((j + 1) * BLK, N)) for j in sel])
+
+
+def sparse_lse_block(qr, kr, mask_row, N: int, BLK: int, scale: float, qb: int) -> np.ndarray:
+    """Natural log-sum-exp of the scaled scores of query block qb's real rows
+    over the keys block-sparse attention uses for them (real tokens of the
+    selected key blocks): lse_i = log sum_k exp(scale * q_i . k), float64
+    [n_real_rows]; -inf for every row when nothing is selected."""
+    lo, hi = qb * BLK, min((qb + 1) * BLK, N)
+    keys = _selected_keys(mask_row, N, BLK)
+    if keys.size == 0:
+        return np.full(hi - lo, -np.inf)
+    logits = (qr[lo:hi].astype(np.float64) @ kr[keys].astype(np.float64).T) * scale
+    m = logits.max(axis=1)
+    return m + np.log(np.exp(logits - m[:, None]).sum(axis=1))
+
+
+def sparse_lse(qr, kr, mask, N: int, BLK: int, scale: float) -> np.ndarray:
+    """sparse_lse_block over every (batch, head, query block): [B, Hh, N] f64,
+    indexed by reordered query position."""
+    B, Hh, Npad, _ = qr.shape
+    nB = Npad // BLK
+    out = np.empty((B, Hh, N), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hh):
+            for i in range(nB):
+                out[b, h, i * BLK:min((i + 1) * BLK, N)] = sparse_lse_block(
+                    qr[b, h], kr[b, h], mask[b, h, i], N, BLK, scale, i)
+    return out
+
+
+def mask_recall(lse_selected, lse_all) -> np.ndarray:
+    """Share of each query's full softmax mass that its selected keys hold:
+    sum_{k selected} exp(s_k) / sum_{all k} exp(s_k) = exp(lse_sel - lse_all)."""
+    return np.exp(np.asarray(lse_selected, np.float64) - np.asarray(lse_all, np.float64))
 
 
 # --------------------------------------------------------------------------

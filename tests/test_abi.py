@@ -85,18 +85,23 @@ def test_validation_errors_before_launch(lib):
     # attention: bad schedule flag, missing workspace, trace without buffer
     big_ws = 1 << 20
     assert lib.fva_sparse_attn(16, 16, 16, 16, 1, 2, 64, ctypes.byref(g), ctypes.byref(m), 0.0,
-                               0x4, 256, big_ws, None, None) == F.FVA_ERR_INVALID_ARG
+                               0x4, 256, big_ws, None, None, None) == F.FVA_ERR_INVALID_ARG
     assert lib.fva_sparse_attn(16, 16, 16, 16, 1, 2, 64, ctypes.byref(g), ctypes.byref(m), 0.0,
-                               0, None, 0, None, None) == F.FVA_ERR_WORKSPACE
+                               0, None, 0, None, None, None) == F.FVA_ERR_WORKSPACE
     assert lib.fva_sparse_attn(16, 16, 16, 16, 1, 2, 64, ctypes.byref(g), ctypes.byref(m), 0.0,
-                               0, 256, 64, None, None) == F.FVA_ERR_WORKSPACE
+                               0, 256, 64, None, None, None) == F.FVA_ERR_WORKSPACE
     assert lib.fva_sparse_attn(16, 16, 16, 16, 1, 2, 64, ctypes.byref(g), ctypes.byref(m), 0.0,
-                               F.FVA_TRACE, 256, big_ws, None, None) == F.FVA_ERR_INVALID_ARG
+                               F.FVA_TRACE, 256, big_ws, None, None, None) == F.FVA_ERR_INVALID_ARG
+    # a log-sum-exp buffer must be 4-byte aligned
+    assert lib.fva_sparse_attn(16, 16, 16, 16, 1, 2, 64, ctypes.byref(g), ctypes.byref(m), 0.0,
+                               0, 256, big_ws, None, 18, None) == F.FVA_ERR_INVALID_ARG
+    assert lib.fva_dense_attn(16, 16, 16, 16, 1, 2, 64, ctypes.byref(g), 0.0, 18, None) == \
+        F.FVA_ERR_INVALID_ARG
     # the XCD schedule caps the number of heads
     many = F.make_grid((2, 8, 8), (1, 8, 8))
     assert lib.fva_sparse_attn(256, 256, 256, 256, 1, 5000, 64, ctypes.byref(many),
                                ctypes.byref(m), 0.0, F.FVA_SCHED_XCD, 256, 1 << 30, None,
-                               None) == F.FVA_ERR_UNSUPPORTED
-    assert lib.fva_dense_attn(16, 16, 0, 16, 1, 2, 64, ctypes.byref(g), 0.0, None) == \
+                               None, None) == F.FVA_ERR_UNSUPPORTED
+    assert lib.fva_dense_attn(16, 16, 0, 16, 1, 2, 64, ctypes.byref(g), 0.0, None, None) == \
         F.FVA_ERR_INVALID_ARG
     assert lib.fva_status_string(F.FVA_ERR_WORKSPACE) == b"FVA_ERR_WORKSPACE"

@@ -305,16 +305,66 @@ def test_dense_attention_matches_oracle_and_full_mask(entry):
     assert torch.equal(buf.orr.view(torch.int16), dense.view(torch.int16))
 
 
+# Per-query log-sum-exp.  The kernels sum bf16-rounded probabilities (each
+# off by at most 2^-9 relative), so log l is within ~2e-3 of the float64 sum;
+# scores differ from the oracle only by float32 accumulation.  Recall is the
+# exponential of a difference of two such values.
+LSE_ABS = 5e-3
+RECALL_ABS = 1e-2
+
+
+@pytest.mark.parametrize("entry", SMALL, ids=[e[0] for e in SMALL])
+def test_lse_and_recall_match_oracle(entry):
+    w = _wl(entry)
+    q, k, v, qd, kd, vd, buf = setup(w)
+    gpu_reorder(buf, qd, kd, vd)
+    qr = O.reorder(q.float().numpy(), w.grid, w.block)
+    kr = O.reorder(k.float().numpy(), w.grid, w.block)
+    r = O.route_path(qr, kr, w.N, w.BLK, w.scale, w.top_p, w.topk_floor, w.aug_budget)
+    route(buf, w, scores_in=r["scores32"])
+    check_mask_exact(buf, r, w.nB)
+    n = w.B * w.Hh * w.N
+    lse = {}
+    for fl in (F.FVA_SCHED_QUEUE, F.FVA_SCHED_XCD):
+        t = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+        F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, buf.grid, buf.mask(),
+                          0.0, fl, buf.attn_ws, buf.sizes.attn_ws_bytes, None, lse=t)
+        lse[fl] = t
+    out_with = buf.orr.clone()
+    attn(buf)
+    lse_d = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    assert torch.equal(buf.orr.view(torch.int16), out_with.view(torch.int16))
+    F.fva_dense_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, buf.grid, lse=lse_d)
+    torch.cuda.synchronize()
+    assert torch.equal(lse[F.FVA_SCHED_QUEUE].view(torch.int32), lse[F.FVA_SCHED_XCD].view(torch.int32))
+    got_s = lse[F.FVA_SCHED_QUEUE].cpu().numpy().astype(np.float64).reshape(w.B, w.Hh, w.N)
+    got_d = lse_d.cpu().numpy().astype(np.float64).reshape(w.B, w.Hh, w.N)
+    ref_s = O.sparse_lse(qr, kr, r["mask"], w.N, w.BLK, w.scale)
+    ref_d = O.sparse_lse(qr, kr, np.ones_like(r["mask"]), w.N, w.BLK, w.scale)
+    fin = np.isfinite(ref_s)
+    assert np.array_equal(np.isfinite(got_s), fin) and np.all(got_s[~fin] == -np.inf)
+    assert np.abs(got_s[fin] - ref_s[fin]).max() <= LSE_ABS
+    assert np.all(np.isfinite(got_d)) and np.abs(got_d - ref_d).max() <= LSE_ABS
+    rec_got, rec_ref = O.mask_recall(got_s, got_d), O.mask_recall(ref_s, ref_d)
+    print(f"{w.name}: lse max_abs={np.abs(got_s[fin] - ref_s[fin]).max():.2e} "
+          f"recall mean={rec_ref.mean():.4f} |diff|max={np.abs(rec_got - rec_ref).max():.2e}")
+    assert np.abs(rec_got - rec_ref).max() <= RECALL_ABS
+
+
 def test_empty_rows_give_zero_output():
     w = SMALL[1][1]
     q, k, v, qd, kd, vd, buf = setup(w)
     gpu_reorder(buf, qd, kd, vd)
     route(buf, w, top_p=0.0, topk=0, aug=0)
     buf.orr.fill_(1.0)
-    attn(buf)
+    lse = torch.zeros(w.B * w.Hh * w.N, dtype=torch.float32, device="cuda")
+    F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, buf.grid, buf.mask(), 0.0,
+                      F.FVA_SCHED_QUEUE, buf.attn_ws, buf.sizes.attn_ws_bytes, None, lse=lse)
     torch.cuda.synchronize()
     assert int(buf.row_count.sum()) == 0
     assert torch.count_nonzero(buf.orr).item() == 0
+    assert bool(torch.all(lse == float("-inf")))
 
 
 def test_full_path_end_to_end_tiny():

@@ -328,6 +328,60 @@ def test_block_indicator_values_measure_block_mass():
     assert np.all(out[0, 0, N:] == 0)
 
 
+def _lse_case(seed, Hh=2, d=16):
+    grid, block = (3, 5, 7), (1, 2, 4)        # N=105, BLK=8, nB=14, ragged tail
+    N, BLK, nB, Npad = O.sizes(*grid, *block)
+    rng = np.random.default_rng(seed)
+    qr = rng.standard_normal((1, Hh, Npad, d))
+    kr = 1.5 * rng.standard_normal((1, Hh, Npad, d))   # garbage in the pad rows too
+    return N, BLK, nB, Npad, qr, kr, rng
+
+
+def test_lse_full_mask_equals_library_logsumexp():
+    import scipy.special
+    N, BLK, nB, Npad, qr, kr, _ = _lse_case(21)
+    full = np.ones((1, 2, nB, nB), dtype=bool)
+    lse = O.sparse_lse(qr, kr, full, N, BLK, 0.3)
+    logits = 0.3 * np.einsum("bhnd,bhmd->bhnm", qr[:, :, :N], kr[:, :, :N])
+    ref = scipy.special.logsumexp(logits, axis=-1)
+    assert lse.shape == (1, 2, N)
+    assert np.abs(lse - ref).max() < 1e-12
+    assert np.abs(O.mask_recall(lse, ref) - 1.0).max() < 1e-12
+
+
+def test_recall_equals_dense_mass_on_selected_blocks():
+    # dense attention with block-indicator values gives each query's softmax
+    # mass per key block; recall of a mask is the sum over its selected blocks
+    N, BLK, nB, Npad, qr, kr, rng = _lse_case(22, Hh=1)
+    vr = np.zeros((1, 1, Npad, qr.shape[-1]))                             # d >= nB columns
+    for r in range(N):
+        vr[0, 0, r, r // BLK] = 1.0
+    full = np.ones((1, 1, nB, nB), dtype=bool)
+    mass = O.sparse_attention(qr, kr, vr, full, N, BLK, 0.4)[0, 0, :N, :nB]  # [N, nB]
+    mask = rng.random((1, 1, nB, nB)) < 0.35
+    mask[0, 0, 3] = False                                                  # a row with nothing
+    rec = O.mask_recall(O.sparse_lse(qr, kr, mask, N, BLK, 0.4),
+                        O.sparse_lse(qr, kr, full, N, BLK, 0.4))[0, 0]
+    row_mask = np.repeat(mask[0, 0], BLK, axis=0)[:N]                      # [N, nB]
+    expect = (mass * row_mask).sum(axis=1)
+    assert np.abs(rec - expect).max() < 1e-12
+    assert np.all(rec[3 * BLK:4 * BLK] == 0.0)
+    assert np.all(rec <= 1.0 + 1e-12)
+
+
+def test_lse_is_logaddexp_of_single_block_lses():
+    N, BLK, nB, Npad, qr, kr, rng = _lse_case(23, Hh=1)
+    mask = rng.random((1, 1, nB, nB)) < 0.5
+    mask[..., nB - 1] = True                                               # include the ragged block
+    lse = O.sparse_lse(qr, kr, mask, N, BLK, 0.25)[0, 0]
+    parts = []
+    for j in range(nB):
+        one = np.zeros_like(mask)
+        one[..., j] = mask[..., j]
+        parts.append(O.sparse_lse(qr, kr, one, N, BLK, 0.25)[0, 0])
+    assert np.abs(lse - np.logaddexp.reduce(np.stack(parts), axis=0)).max() < 1e-12
+
+
 def test_zero_queries_average_selected_real_values():
     grid, block = (3, 5, 7), (1, 2, 4)
     N, BLK, nB, Npad = O.sizes(*grid, *block)

@@ -63,6 +63,24 @@ MUTANTS = [
      [("test_hilbert_curve_is_a_face_adjacent_walk_of_the_cube", {"bits": 3})]),
     ("Hilbert tiles in raster order", "    return sorted(ids, key=lambda i: key[i])",
      "    return ids", ["test_hilbert_tile_order_restricts_the_cube_walk"]),
+    ("lse keeps padded keys",
+     "    return np.concatenate([np.arange(j * BLK, min((j + 1) * BLK, N)) for j in sel])",
+     "    return np.concatenate([np.arange(j * BLK, (j + 1) * BLK) for j in sel])",
+     ["test_lse_full_mask_equals_library_logsumexp"]),
+    ("lse forgets to add the max back",
+     "return m + np.log(np.exp(logits - m[:, None]).sum(axis=1))",
+     "return np.log(np.exp(logits - m[:, None]).sum(axis=1))",
+     ["test_lse_full_mask_equals_library_logsumexp"]),
+    ("lse reads the first query rows",
+     "logits = (qr[lo:hi].astype(np.float64) @ kr[keys]",
+     "logits = (qr[:hi - lo].astype(np.float64) @ kr[keys]",
+     ["test_lse_full_mask_equals_library_logsumexp"]),
+    ("lse drops the scale", "@ kr[keys].astype(np.float64).T) * scale",
+     "@ kr[keys].astype(np.float64).T)", ["test_lse_full_mask_equals_library_logsumexp"]),
+    ("recall inverted",
+     "np.exp(np.asarray(lse_selected, np.float64) - np.asarray(lse_all, np.float64))",
+     "np.exp(np.asarray(lse_all, np.float64) - np.asarray(lse_selected, np.float64))",
+     ["test_recall_equals_dense_mass_on_selected_blocks"]),
 ]
 
 
