@@ -8,7 +8,10 @@ For every full workload:
     differing row is a near-tie of the cut in the oracle;
   * attention output on a sample of query blocks (heaviest, lightest, the
     ragged last block of a head, seeded random ones) is within max-abs 2e-2
-    and mean-relative 5e-3 of the oracle, computed block by block.
+    and mean-relative 5e-3 of the oracle, computed block by block;
+  * on the same blocks the sparse and dense per-query log-sum-exp are within
+    5e-3 of the oracle and the mask recall exp(lse_sparse - lse_dense) within
+    1e-2 (bf16-rounded probabilities are summed, each within 2^-9 relative).
 """
 
 import numpy as np
@@ -23,6 +26,8 @@ pytestmark = pytest.mark.gpu
 
 MAX_ABS = 2e-2
 MEAN_REL = 5e-3
+LSE_ABS = 5e-3
+RECALL_ABS = 1e-2
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -99,8 +104,11 @@ def run_case(w, n_random=12):
         assert np.all(hc == np.maximum(routed, np.minimum(w.aug_budget, w.nB * w.nB)))
 
     print(f"[{w.name}] attention (XCD schedule) on sampled query blocks", flush=True)
+    nq = w.B * w.Hh * w.N
+    lse_s = torch.full((nq,), float("nan"), dtype=torch.float32, device="cuda")
+    lse_d = torch.full((nq,), float("nan"), dtype=torch.float32, device="cuda")
     F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, buf.grid, buf.mask(),
-                      0.0, F.FVA_SCHED_XCD, buf.attn_ws, buf.sizes.attn_ws_bytes)
+                      0.0, F.FVA_SCHED_XCD, buf.attn_ws, buf.sizes.attn_ws_bytes, lse=lse_s)
     torch.cuda.synchronize()
     rows = set()
     counts = r["counts"].reshape(-1)
@@ -124,6 +132,27 @@ def run_case(w, n_random=12):
     print(f"[{w.name}] {len(items)} blocks: max_abs={mx:.3e} mean_rel={num / den:.3e}",
           flush=True)
     assert mx <= MAX_ABS and num / den <= MEAN_REL
+
+    print(f"[{w.name}] log-sum-exp and recall on the same blocks", flush=True)
+    F.fva_dense_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, buf.grid, lse=lse_d)
+    torch.cuda.synchronize()
+    gs = lse_s.cpu().numpy().astype(np.float64).reshape(w.B, w.Hh, w.N)
+    gd = lse_d.cpu().numpy().astype(np.float64).reshape(w.B, w.Hh, w.N)
+    full_row = np.ones(w.nB, dtype=bool)
+    e_lse = e_rec = 0.0
+    for (b, h, i) in items:
+        lo, hi = i * w.BLK, min((i + 1) * w.BLK, w.N)
+        ref_s = O.sparse_lse_block(qr[b, h], kr[b, h], r["mask"][b, h, i], w.N, w.BLK, w.scale, i)
+        ref_d = O.sparse_lse_block(qr[b, h], kr[b, h], full_row, w.N, w.BLK, w.scale, i)
+        fin = np.isfinite(ref_s)
+        assert np.array_equal(np.isfinite(gs[b, h, lo:hi]), fin)
+        if fin.any():
+            e_lse = max(e_lse, float(np.abs(gs[b, h, lo:hi][fin] - ref_s[fin]).max()))
+        e_lse = max(e_lse, float(np.abs(gd[b, h, lo:hi] - ref_d).max()))
+        rec = O.mask_recall(gs[b, h, lo:hi], gd[b, h, lo:hi])
+        e_rec = max(e_rec, float(np.abs(rec - O.mask_recall(ref_s, ref_d)).max()))
+    print(f"[{w.name}] lse max_abs={e_lse:.2e} recall max_abs={e_rec:.2e}", flush=True)
+    assert e_lse <= LSE_ABS and e_rec <= RECALL_ABS
 
 
 @pytest.mark.parametrize("name", ["480p", "720p", "hetero", "long720p"])
