@@ -373,6 +373,34 @@ def main():
         torch.cuda.synchronize()
         recall["topk_fixed_raster"] = recall_stats(lse_sel, lse_all)
         extras["fixed_topk_control"] = fk
+        # quality-efficiency points: Top-p at several p (floor as configured)
+        # and, for each, a fixed Top-k with the same executed work
+        pareto = []
+        for p_cut in (0.8, 0.9, 0.95, 0.98):
+            for policy in ("top_p", "top_k"):
+                if policy == "top_p":
+                    prm_x = F.fva_route_params(p_cut, w.topk_floor, 0, 0.0, 0)
+                else:
+                    prm_x = F.fva_route_params(0.0, kmatch, 0, 0.0, 0)
+                F.fva_route(buf.qr, buf.kr, w.B, w.Hh, w.d, g, prm_x, m, buf.route_ws,
+                            buf.sizes.route_ws_bytes, 0)
+                x0, x1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                x0.record(stream)
+                F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, g, m, 0.0,
+                                  args.sched, buf.attn_ws, buf.sizes.attn_ws_bytes, None,
+                                  lse=lse_sel)
+                x1.record(stream)
+                torch.cuda.synchronize()
+                xnnz = int(buf.row_count.sum().item())
+                if policy == "top_p":
+                    kmatch = int(round(xnnz / (w.B * w.Hh * w.nB)))
+                rs = recall_stats(lse_sel, lse_all)
+                pareto.append({"policy": policy,
+                               "param": p_cut if policy == "top_p" else kmatch,
+                               "density": round(xnnz / (w.B * w.Hh * w.nB ** 2), 4),
+                               "recall_mean": rs["mean"], "recall_p05": rs["p05"],
+                               "attn_ms": round(x0.elapsed_time(x1), 3)})
+        recall["pareto_raster"] = pareto
         # restore the raster-order Top-p state for what follows
         step(False)
         torch.cuda.synchronize()
