@@ -129,8 +129,18 @@ def cpu_baseline(w, q, k, v, seconds):
         if time.perf_counter() - ts >= seconds and n >= 4:
             break
     dt = time.perf_counter() - ts
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "cpu_model": cpu_model,
         "sample": (f"float64 numpy oracle, attention of {n} seeded-random (head, query-block) "
                    f"items of the {w.name} workload ({flops / 1e12:.3f} executed TFLOP in "
                    f"{dt:.1f} s); its reorder of Q,K,V took {t1 - t0:.1f} s and routing of all "
