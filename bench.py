@@ -160,6 +160,30 @@ def recall_stats(lse_sel, lse_all):
             "min": round(float(r.min()), 5)}
 
 
+def copy_reference(reorder_gbs, mib=2048, reps=10):
+    """Practical HBM rate of this card: a plain device-to-device copy (torch),
+    counted as bytes read plus bytes written, the reference the streaming
+    kernels (reorder, pool, un-reorder) are read against."""
+    import torch
+
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2.0 * n / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    del src, dst
+    return {"what": f"torch device copy of {mib} MiB, read + write bytes", "GBs": round(gbs, 1),
+            "frac_of_8TBs": round(gbs / 8000.0, 4), "reorder_over_copy": round(reorder_gbs / gbs, 4)}
+
+
 def gemm_reference(attn_tflops, n=8192, reps=50):
     """Practical bf16 MFMA rate of this card: the vendor GEMM (torch.matmul)
     on random normal operands.  Data-dependent power, not the issue rate, sets
@@ -291,6 +315,7 @@ def main():
         extras["dense_tflops"] = de_flop / (ms_dense * 1e-3) / 1e12
         extras["speedup_vs_dense"] = ms_dense / ms_attn
         extras["gemm_reference"] = gemm_reference(attn_tflops)
+        extras["torch_copy_reference"] = copy_reference(reorder_bytes / (ms_reorder * 1e-3) / 1e9)
         # mask recall: per-query log-sum-exp of the sparse and the dense kernel
         nq = w.B * w.Hh * w.N
         lse_all = torch.empty(nq, dtype=torch.float32, device="cuda")
