@@ -34,6 +34,13 @@ SMALL = [
     ("short-tail-d64-b128", small_workload("short-tail-d64-b128", 2, 64, (2, 12, 14), (1, 8, 16), 0.9, 1)),
     ("topup-d128-b128", small_workload("topup-d128-b128", 3, 128, (4, 10, 24), (2, 8, 8), 0.6, 1,
                                        aug_budget=40, amp=(4.0, 0.3, 2.0))),
+    # degenerate shapes: one real token in one block; exactly one full block
+    # with no floor; one block plus a single-token clipped tile
+    ("single-token-d128-b128", small_workload("single-token-d128-b128", 2, 128, (1, 1, 1),
+                                              (1, 8, 16), 0.9, 1)),
+    ("one-block-d64-b64", small_workload("one-block-d64-b64", 3, 64, (1, 8, 8), (1, 8, 8), 0.5, 0)),
+    ("block-plus-one-d128-b128", small_workload("block-plus-one-d128-b128", 2, 128, (1, 1, 129),
+                                                (1, 1, 128), 0.9, 1)),
 ]
 
 
