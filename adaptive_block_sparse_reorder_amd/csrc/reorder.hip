@@ -33,17 +33,29 @@ __global__ __launch_bounds__(kThreads) void reorder_rows_fwd(
   __syncthreads();
   const int cpr = d >> 3;  // 16-byte chunks per row
   const int total = kRows * Hh * cpr;
-  for (int L = threadIdx.x; L < total; L += kThreads) {
-    const int c = L % cpr;
-    const int rh = L / cpr;
-    const int h = rh % Hh;
-    const int rl = rh / Hh;
-    const int64_t r = r0 + rl;
-    if (r >= Npad) continue;
-    const int64_t n = tok[rl];
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (n >= 0) v = *(const u32x4*)(src + b * sb + n * sn + h * sh + c * 8);
-    *(u32x4*)(dst + (((int64_t)b * Hh + h) * Npad + r) * d + c * 8) = v;
+  // four independent 16-byte loads in flight per thread; the inputs are read
+  // once, so they are loaded non-temporally
+  for (int L0 = threadIdx.x; L0 < total; L0 += 4 * kThreads) {
+    u32x4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int L = L0 + j * kThreads;
+      v[j] = u32x4{0u, 0u, 0u, 0u};
+      if (L < total) {
+        const int c = L % cpr, rh = L / cpr, h = rh % Hh, rl = rh / Hh;
+        const int64_t n = tok[rl];
+        if (n >= 0) v[j] = __builtin_nontemporal_load((const u32x4*)(src + b * sb + n * sn + h * sh + c * 8));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int L = L0 + j * kThreads;
+      if (L >= total) continue;
+      const int c = L % cpr, rh = L / cpr, h = rh % Hh, rl = rh / Hh;
+      const int64_t r = r0 + rl;
+      if (r >= Npad) continue;
+      *(u32x4*)(dst + (((int64_t)b * Hh + h) * Npad + r) * d + c * 8) = v[j];
+    }
   }
 }
 
@@ -101,12 +113,22 @@ __global__ __launch_bounds__(kThreads) void reorder_tile64_fwd(
   }
   __syncthreads();
   constexpr int cpr = D / 8;
-  for (int L = threadIdx.x; L < 64 * cpr; L += kThreads) {
+  constexpr int kPer = 64 * cpr / kThreads;  // 16-byte loads per thread (4 at d=128)
+  static_assert(kPer * kThreads == 64 * cpr, "chunk size");
+  u32x4 lv[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int L = threadIdx.x + j * kThreads;
     const int c = L % cpr, k = L / cpr;
     const int64_t n = tok[k];
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (n >= 0) v = *(const u32x4*)(src + b * sb + n * sn + h * sh + c * 8);
-    *(u32x4*)(&stage[k * kPitch + c * 8]) = v;
+    lv[j] = u32x4{0u, 0u, 0u, 0u};
+    if (n >= 0) lv[j] = __builtin_nontemporal_load((const u32x4*)(src + b * sb + n * sn + h * sh + c * 8));
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int L = threadIdx.x + j * kThreads;
+    const int c = L % cpr, k = L / cpr;
+    *(u32x4*)(&stage[k * kPitch + c * 8]) = lv[j];
   }
   __syncthreads();
   u32x4* out = (u32x4*)(dst + ((int64_t)bh * (Npad / 64) + chunk) * (int64_t)D * 64);
