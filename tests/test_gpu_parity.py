@@ -556,3 +556,62 @@ def test_softmax_reference_moves_with_logit_ramps(slope):
     torch.cuda.synchronize()
     mx, rel = err_stats(to_np(buf.orr)[:, :, :N], ref[:, :, :N])
     assert mx <= MAX_ABS and rel <= MEAN_REL
+
+
+# ----------------------------------------------------------- seeded shape sweep
+
+_BLOCKS = [(1, 8, 8), (1, 8, 16), (2, 8, 8), (1, 4, 16), (2, 4, 8), (1, 16, 8), (4, 4, 4),
+           (2, 8, 4)]
+
+
+def _random_workload(seed):
+    """A small workload with shape, head dim, block, cut, floor, amplitudes and
+    top-up budget drawn from a seeded generator."""
+    rng = np.random.default_rng(1000 + seed)
+    block = _BLOCKS[int(rng.integers(len(_BLOCKS)))]
+    grid = (int(rng.integers(1, 5)), int(rng.integers(1, 33)), int(rng.integers(1, 49)))
+    d = int(rng.choice([64, 128]))
+    Hh = int(rng.integers(1, 5))
+    p = float(rng.choice([0.3, 0.6, 0.9, 0.97, 1.0]))
+    k = int(rng.integers(0, 5))
+    N = grid[0] * grid[1] * grid[2]
+    BLK = block[0] * block[1] * block[2]
+    nB = -(-N // BLK)
+    aug = int(rng.integers(0, nB * nB + 1)) if rng.random() < 0.3 else 0
+    amp = tuple(float(x) for x in rng.uniform(0.0, 4.0, size=Hh))
+    return small_workload(f"rand{seed}", Hh, d, grid, block, p, k, aug_budget=aug, amp=amp,
+                          seed=seed)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes_full_path(seed):
+    w = _random_workload(seed)
+    print(f"rand{seed}: Hh={w.Hh} d={w.d} grid={w.grid} block={w.block} N={w.N} nB={w.nB} "
+          f"p={w.top_p} k={w.topk_floor} aug={w.aug_budget}", flush=True)
+    q, k, v, qd, kd, vd, buf = setup(w)
+    gpu_reorder(buf, qd, kd, vd)
+    qr = O.reorder(q.float().numpy(), w.grid, w.block)
+    kr = O.reorder(k.float().numpy(), w.grid, w.block)
+    vr = O.reorder(v.float().numpy(), w.grid, w.block)
+    r = O.route_path(qr, kr, w.N, w.BLK, w.scale, w.top_p, w.topk_floor, w.aug_budget)
+    route(buf, w, scores_in=r["scores32"])
+    check_mask_exact(buf, r, w.nB)
+    assert np.array_equal(buf.row_count.cpu().numpy(), r["counts"].reshape(-1))
+    assert np.array_equal(buf.head_count.cpu().numpy(), r["head_count"].reshape(-1))
+    n = w.B * w.Hh * w.N
+    lse = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    buf.orr.fill_(float("nan"))
+    F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, buf.grid, buf.mask(), 0.0,
+                      F.FVA_SCHED_XCD, buf.attn_ws, buf.sizes.attn_ws_bytes, None, lse=lse)
+    torch.cuda.synchronize()
+    ref = O.sparse_attention(qr, kr, vr, r["mask"], w.N, w.BLK, w.scale)
+    got = to_np(buf.orr)
+    mx, rel = err_stats(got[:, :, :w.N], ref[:, :, :w.N])
+    assert mx <= MAX_ABS and rel <= MEAN_REL, (mx, rel)
+    assert np.all(got[:, :, w.N:] == 0)
+    ref_lse = O.sparse_lse(qr, kr, r["mask"], w.N, w.BLK, w.scale)
+    got_lse = lse.cpu().numpy().astype(np.float64).reshape(w.B, w.Hh, w.N)
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(got_lse), fin)
+    if fin.any():
+        assert np.abs(got_lse[fin] - ref_lse[fin]).max() <= LSE_ABS
