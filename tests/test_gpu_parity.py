@@ -586,13 +586,23 @@ def _random_workload(seed):
 @pytest.mark.parametrize("seed", range(24))
 def test_random_shapes_full_path(seed):
     w = _random_workload(seed)
+    order = "hilbert" if seed % 3 == 2 else "raster"
     print(f"rand{seed}: Hh={w.Hh} d={w.d} grid={w.grid} block={w.block} N={w.N} nB={w.nB} "
-          f"p={w.top_p} k={w.topk_floor} aug={w.aug_budget}", flush=True)
+          f"p={w.top_p} k={w.topk_floor} aug={w.aug_budget} order={order}", flush=True)
     q, k, v, qd, kd, vd, buf = setup(w)
-    gpu_reorder(buf, qd, kd, vd)
-    qr = O.reorder(q.float().numpy(), w.grid, w.block)
-    kr = O.reorder(k.float().numpy(), w.grid, w.block)
-    vr = O.reorder(v.float().numpy(), w.grid, w.block)
+    g = buf.grid
+    table = F.tile_table(g, F.FVA_ORDER_HILBERT) if order == "hilbert" else None
+    for x, dst, lay in ((qd, buf.qr, F.FVA_LAYOUT_ROWS), (kd, buf.kr, F.FVA_LAYOUT_K64),
+                        (vd, buf.vt, F.FVA_LAYOUT_V64)):
+        F.fva_reorder_ex(x, dst, w.B, w.Hh, w.d, g, table, F.token_strides(x), F.FVA_FORWARD, lay)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(buf.qr), O.reorder(q.view(torch.int16).numpy(), w.grid, w.block,
+                                                  order))
+    assert np.array_equal(bits(buf.kr), k64_expected(
+        O.reorder(k.view(torch.int16).numpy(), w.grid, w.block, order)))
+    qr = O.reorder(q.float().numpy(), w.grid, w.block, order)
+    kr = O.reorder(k.float().numpy(), w.grid, w.block, order)
+    vr = O.reorder(v.float().numpy(), w.grid, w.block, order)
     r = O.route_path(qr, kr, w.N, w.BLK, w.scale, w.top_p, w.topk_floor, w.aug_budget)
     route(buf, w, scores_in=r["scores32"])
     check_mask_exact(buf, r, w.nB)
@@ -601,14 +611,20 @@ def test_random_shapes_full_path(seed):
     n = w.B * w.Hh * w.N
     lse = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
     buf.orr.fill_(float("nan"))
-    F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, buf.grid, buf.mask(), 0.0,
+    F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, g, buf.mask(), 0.0,
                       F.FVA_SCHED_XCD, buf.attn_ws, buf.sizes.attn_ws_bytes, None, lse=lse)
+    out = torch.empty_like(qd)
+    F.fva_reorder_ex(buf.orr, out, w.B, w.Hh, w.d, g, table, F.token_strides(out), F.FVA_INVERSE)
     torch.cuda.synchronize()
     ref = O.sparse_attention(qr, kr, vr, r["mask"], w.N, w.BLK, w.scale)
     got = to_np(buf.orr)
     mx, rel = err_stats(got[:, :, :w.N], ref[:, :, :w.N])
     assert mx <= MAX_ABS and rel <= MEAN_REL, (mx, rel)
     assert np.all(got[:, :, w.N:] == 0)
+    # the inverse reorder returns the same values to token order
+    ref_tok = O.unreorder(ref, w.grid, w.block, order)
+    mx2, rel2 = err_stats(to_np(out), ref_tok)
+    assert mx2 <= MAX_ABS and rel2 <= MEAN_REL, (mx2, rel2)
     ref_lse = O.sparse_lse(qr, kr, r["mask"], w.N, w.BLK, w.scale)
     got_lse = lse.cpu().numpy().astype(np.float64).reshape(w.B, w.Hh, w.N)
     fin = np.isfinite(ref_lse)
