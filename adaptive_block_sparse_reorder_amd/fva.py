@@ -344,11 +344,12 @@ def token_strides(x) -> Sequence[int]:
 
 def forward(buf: Buffers, q, k, v, top_p: float, topk_floor: int, aug_budget: int = 0,
             scale: float = 0.0, route_flags: int = 0, attn_flags: int = FVA_SCHED_XCD,
-            stream=None, table=None):
+            stream=None, table=None, lse=None):
     """One pass of the hot path: reorder Q (rows), K (k64), V (v64) -> route -> block-sparse
     attention -> inverse reorder.  Inputs [B, N, Hh, d] bf16 on the device;
     the result lands in buf.out.  `table`: a device tile table from
-    fva_tile_order (None = raster tile order)."""
+    fva_tile_order (None = raster tile order).  `lse`: optional float32 device
+    tensor of B*Hh*N entries for each query's log-sum-exp (reordered positions)."""
     g, B, Hh, d = buf.grid, buf.B, buf.Hh, buf.d
     fva_reorder_ex(q, buf.qr, B, Hh, d, g, table, token_strides(q), FVA_FORWARD,
                    FVA_LAYOUT_ROWS, stream)
@@ -362,7 +363,7 @@ def forward(buf: Buffers, q, k, v, top_p: float, topk_floor: int, aug_budget: in
               route_flags, stream)
     fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, B, Hh, d, g, m, scale, attn_flags,
                     buf.attn_ws, buf.sizes.attn_ws_bytes,
-                    buf.trace if (attn_flags & FVA_TRACE) else None, stream)
+                    buf.trace if (attn_flags & FVA_TRACE) else None, stream, lse=lse)
     fva_reorder_ex(buf.orr, buf.out, B, Hh, d, g, table, token_strides(buf.out), FVA_INVERSE,
                    FVA_LAYOUT_ROWS, stream)
     return buf.out

@@ -377,7 +377,8 @@ def test_empty_rows_give_zero_output():
 def test_full_path_end_to_end_tiny():
     w = WORKLOADS["tiny"]
     q, k, v, qd, kd, vd, buf = setup(w)
-    F.forward(buf, qd, kd, vd, w.top_p, w.topk_floor, w.aug_budget)
+    lse = torch.full((w.B * w.Hh * w.N,), float("nan"), dtype=torch.float32, device="cuda")
+    F.forward(buf, qd, kd, vd, w.top_p, w.topk_floor, w.aug_budget, lse=lse)
     torch.cuda.synchronize()
     o_ref, r = O.forward(q.float().numpy(), k.float().numpy(), v.float().numpy(), w.grid,
                          w.block, w.top_p, w.topk_floor, w.aug_budget)
@@ -385,6 +386,10 @@ def test_full_path_end_to_end_tiny():
     assert np.array_equal(got, r["mask"].reshape(-1, w.nB))
     mx, rel = err_stats(to_np(buf.out), o_ref)
     assert mx <= MAX_ABS and rel <= MEAN_REL
+    qr = O.reorder(q.float().numpy(), w.grid, w.block)
+    kr = O.reorder(k.float().numpy(), w.grid, w.block)
+    ref_lse = O.sparse_lse(qr, kr, r["mask"], w.N, w.BLK, w.scale).reshape(-1)
+    assert np.abs(lse.cpu().numpy().astype(np.float64) - ref_lse).max() <= LSE_ABS
 
 
 def test_trace_covers_every_item_once():
