@@ -440,19 +440,22 @@ def main():
         step(False)
         torch.cuda.synchronize()
 
-    # runtime load balancing on 8 virtual ranks from the realized workloads
+    # runtime load balancing on 8 virtual ranks (fewer when there are fewer
+    # heads) from the realized workloads
+    vranks = min(8, len(buf.head_count))
     hc = buf.head_count.cpu().numpy().astype(np.int64).tolist()
     rlb = {}
     for name, topo in (("pairs", F.FVA_RLB_PAIRS), ("ring", F.FVA_RLB_RING)):
-        _, _, roh, st = F.fva_rlb_plan(hc, 8, topo)
+        _, _, roh, st = F.fva_rlb_plan(hc, vranks, topo)
         rlb[name] = {"lambda_before": round(st.lambda_before, 4),
                      "lambda_after": round(st.lambda_after, 4),
                      "migrations": int(st.migrations), "solve_us": round(st.solve_us, 1)}
         if name == "pairs":
             roh_pairs = roh
-    extras["rlb_8_virtual_ranks"] = rlb
+    rlb["ranks"] = vranks
+    extras["rlb_virtual_ranks"] = rlb
     # slack-aware augmentation after balancing (alpha 0.5), applied on the device
-    budgets, rank_after = F.fva_sasa_budget(hc, 8, roh_pairs, 0.5, w.nB * w.nB)
+    budgets, rank_after = F.fva_sasa_budget(hc, vranks, roh_pairs, 0.5, w.nB * w.nB)
     dev_budgets = torch.tensor(budgets, dtype=torch.int64, device="cuda")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
