@@ -105,3 +105,31 @@ def test_validation_errors_before_launch(lib):
     assert lib.fva_dense_attn(16, 16, 0, 16, 1, 2, 64, ctypes.byref(g), 0.0, None, None) == \
         F.FVA_ERR_INVALID_ARG
     assert lib.fva_status_string(F.FVA_ERR_WORKSPACE) == b"FVA_ERR_WORKSPACE"
+
+
+def test_tile_table_sizes_and_limits(lib):
+    # the documented layout: {ntiles, order, 0, 0}, ntiles raster ids, ntiles + 1 starts
+    g = F.make_grid((3, 13, 19), (1, 8, 8))          # 3 x 2 x 3 = 18 tiles, clipped in y and x
+    nbytes = ctypes.c_size_t(0)
+    assert lib.fva_tile_order_bytes(ctypes.byref(g), ctypes.byref(nbytes)) == F.FVA_OK
+    need = nbytes.value
+    assert need == 16 + 4 * 18 + 4 * 19
+    assert lib.fva_tile_order_bytes(ctypes.byref(g), None) == F.FVA_ERR_INVALID_ARG
+    # heavy clipping: 15000 frames of a 1 x 17 strip with 1x8x16 tiles give 30000
+    # tiles but only 1993 blocks, past the tile table's 8192-tile capacity
+    many = F.make_grid((15000, 1, 17), (1, 8, 16))
+    s = F.fva_sizes(many, 1, 1, 64)
+    assert s.nB == 1993
+    assert lib.fva_tile_order_bytes(ctypes.byref(many), ctypes.byref(nbytes)) == \
+        F.FVA_ERR_UNSUPPORTED
+    assert lib.fva_tile_order(ctypes.byref(many), F.FVA_ORDER_HILBERT, 256, 1 << 20, None) == \
+        F.FVA_ERR_UNSUPPORTED
+    st = (ctypes.c_int64 * 3)(64, 64, 64)
+    assert lib.fva_reorder_ex(256, 512, 1, 1, 64, ctypes.byref(many), 1024, st, F.FVA_FORWARD,
+                              F.FVA_LAYOUT_ROWS, None) == F.FVA_ERR_UNSUPPORTED
+    # table too small, unknown order, misaligned table: rejected before any launch
+    assert lib.fva_tile_order(ctypes.byref(g), F.FVA_ORDER_HILBERT, 256, need - 4, None) == \
+        F.FVA_ERR_WORKSPACE
+    assert lib.fva_tile_order(ctypes.byref(g), 7, 256, 1 << 20, None) == F.FVA_ERR_INVALID_ARG
+    assert lib.fva_tile_order(ctypes.byref(g), F.FVA_ORDER_HILBERT, 264, 1 << 20, None) == \
+        F.FVA_ERR_INVALID_ARG
