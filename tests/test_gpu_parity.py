@@ -636,3 +636,27 @@ def test_random_shapes_full_path(seed):
     assert np.array_equal(np.isfinite(got_lse), fin)
     if fin.any():
         assert np.abs(got_lse[fin] - ref_lse[fin]).max() <= LSE_ABS
+
+
+def test_hilbert_table_near_capacity():
+    # 4000 frames of a 1 x 17 strip with 1x8x16 tiles: 8000 clipped tiles, near
+    # the table's 8192-tile capacity, and 532 blocks
+    w = small_workload("strip", 1, 64, (4000, 1, 17), (1, 8, 16), 0.9, 1)
+    q, k, v, qd, kd, vd, buf = setup(w)
+    table = F.tile_table(buf.grid, F.FVA_ORDER_HILBERT)
+    torch.cuda.synchronize()
+    nt = int(np.prod(O.tile_grid(*w.grid, *w.block)))
+    assert nt == 8000
+    t = table.cpu().numpy()
+    assert t[0] == nt and t[1] == F.FVA_ORDER_HILBERT
+    assert t[4:4 + nt].tolist() == O.tile_order(*w.grid, *w.block, "hilbert")
+    starts = t[4 + nt:4 + 2 * nt + 1]
+    assert starts[0] == 0 and starts[-1] == w.N and np.all(np.diff(starts) > 0)
+    F.fva_reorder_ex(qd, buf.qr, w.B, w.Hh, w.d, buf.grid, table, F.token_strides(qd))
+    out = torch.empty_like(qd)
+    F.fva_reorder_ex(buf.qr, out, w.B, w.Hh, w.d, buf.grid, table, F.token_strides(out),
+                     F.FVA_INVERSE)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(buf.qr), O.reorder(q.view(torch.int16).numpy(), w.grid, w.block,
+                                                  "hilbert"))
+    assert torch.equal(out.cpu().view(torch.int16), q.view(torch.int16))
