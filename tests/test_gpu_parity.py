@@ -660,3 +660,35 @@ def test_hilbert_table_near_capacity():
     assert np.array_equal(bits(buf.qr), O.reorder(q.view(torch.int16).numpy(), w.grid, w.block,
                                                   "hilbert"))
     assert torch.equal(out.cpu().view(torch.int16), q.view(torch.int16))
+
+
+def test_xcd_plan_at_its_head_limit():
+    # 4096 heads (the XCD plan's capacity) of 4 blocks each: the plan sorts every
+    # head's W_h in one workgroup; rows are checked against the oracle and the
+    # queue schedule, and the trace shows every item processed once
+    from adaptive_block_sparse_reorder_amd.inputs import Workload
+    w = Workload("heads4096", 1, 4096, 64, (1, 16, 16), (1, 8, 8), 0.8, 1)
+    q, k, v, qd, kd, vd, buf = setup(w)
+    gpu_reorder(buf, qd, kd, vd)
+    qr = O.reorder(q.float().numpy(), w.grid, w.block)
+    kr = O.reorder(k.float().numpy(), w.grid, w.block)
+    vr = O.reorder(v.float().numpy(), w.grid, w.block)
+    r = O.route_path(qr, kr, w.N, w.BLK, w.scale, w.top_p, w.topk_floor, w.aug_budget)
+    route(buf, w, scores_in=r["scores32"])
+    check_mask_exact(buf, r, w.nB)
+    hc = r["head_count"].reshape(-1)
+    assert np.array_equal(buf.head_count.cpu().numpy(), hc) and hc.min() < hc.max()
+    attn(buf, F.FVA_SCHED_XCD)
+    torch.cuda.synchronize()
+    xcd = buf.orr.clone()
+    ref = O.sparse_attention(qr, kr, vr, r["mask"], w.N, w.BLK, w.scale)
+    mx, rel = err_stats(to_np(xcd)[:, :, :w.N], ref[:, :, :w.N])
+    assert mx <= MAX_ABS and rel <= MEAN_REL, (mx, rel)
+    attn(buf, F.FVA_SCHED_QUEUE)
+    torch.cuda.synchronize()
+    assert torch.equal(buf.orr.view(torch.int16), xcd.view(torch.int16))
+    buf.trace.zero_()
+    attn(buf, F.FVA_SCHED_XCD | F.FVA_TRACE)
+    torch.cuda.synchronize()
+    tr = buf.trace.cpu().numpy().view(np.uint32).reshape(-1, 8)[:buf.sizes.rows]
+    assert sorted(tr[:, 0].tolist()) == list(range(int(buf.sizes.rows)))
