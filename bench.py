@@ -74,7 +74,9 @@ def log(msg):
 
 
 def lambda_cu(trace_u32, rows, slots=512):
-    """Imbalance of one traced launch.
+    """Imbalance of one traced launch: the load-imbalance factor of the FVAttn
+    page (papers.paperslantern.ai/papers/2607.16190, section 2: maximum over
+    mean realized load), taken over CUs and over workgroup slots of one GPU.
 
     lambda_cu:   per-CU busy time (sum of its item durations), max/mean over CUs.
     lambda_slot: critical path over mean slot load, span * slots / sum of item
@@ -151,7 +153,10 @@ def cpu_baseline(w, q, k, v, seconds):
 
 def recall_stats(lse_sel, lse_all):
     """Share of each query's full softmax mass held by its selected blocks,
-    exp(lse_sel - lse_all), over every real query of every head."""
+    exp(lse_sel - lse_all), over every real query of every head: the mask
+    coverage the FVAttn page's sections 1 and 3.3 argue about, measured as the
+    attention recall that the DFSAttn abstract listed at
+    thelatestinai.com/papers/2607.16190 uses for block-sparse masks."""
     import torch
 
     r = torch.exp(lse_sel.double() - lse_all.double())
