@@ -293,7 +293,7 @@ def test_sparse_attention_matches_oracle(entry):
         assert torch.equal(outs[fl].view(torch.int16), outs[F.FVA_SCHED_QUEUE].view(torch.int16))
 
 
-@pytest.mark.parametrize("entry", SMALL[:4], ids=[e[0] for e in SMALL[:4]])
+@pytest.mark.parametrize("entry", SMALL, ids=[e[0] for e in SMALL])
 def test_dense_attention_matches_oracle_and_full_mask(entry):
     w = _wl(entry)
     q, k, v, qd, kd, vd, buf = setup(w)
