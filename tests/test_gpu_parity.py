@@ -692,3 +692,47 @@ def test_xcd_plan_at_its_head_limit():
     torch.cuda.synchronize()
     tr = buf.trace.cpu().numpy().view(np.uint32).reshape(-1, 8)[:buf.sizes.rows]
     assert sorted(tr[:, 0].tolist()) == list(range(int(buf.sizes.rows)))
+
+
+def test_forward_replays_under_hip_graph_capture():
+    # the step issues only kernel launches (no host synchronization, no memset),
+    # so one forward() can be captured into a HIP graph and replayed; every
+    # replay, with eager work and synchronizations in between, must reproduce
+    # the eager result, also after new inputs are copied into the captured buffers
+    w = SMALL[3][1]
+    q, k, v, qd, kd, vd, buf = setup(w)
+    F.forward(buf, qd, kd, vd, w.top_p, w.topk_floor, w.aug_budget)
+    torch.cuda.synchronize()
+    ref = [buf.out.clone(), buf.bitmask.clone(), buf.row_count.clone(), buf.queue.clone()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        F.forward(buf, qd, kd, vd, w.top_p, w.topk_floor, w.aug_budget)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        F.forward(buf, qd, kd, vd, w.top_p, w.topk_floor, w.aug_budget)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        buf.out.fill_(float("nan"))
+        buf.bitmask.zero_()
+        buf.queue.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [buf.out, buf.bitmask, buf.row_count, buf.queue]
+        for a, b in zip(got, ref):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b), rep
+    # new inputs in the captured buffers: the replay equals an eager pass on them
+    q2, k2, v2 = make_qkv(w, seed=5)
+    qd.copy_(q2.cuda()); kd.copy_(k2.cuda()); vd.copy_(v2.cuda())
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    buf2 = F.alloc_buffers(w.grid, w.block, w.B, w.Hh, w.d)
+    F.forward(buf2, qd, kd, vd, w.top_p, w.topk_floor, w.aug_budget)
+    torch.cuda.synchronize()
+    assert torch.equal(buf.out.view(torch.int16), buf2.out.view(torch.int16))
+    assert torch.equal(buf.bitmask, buf2.bitmask)
