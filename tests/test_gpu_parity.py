@@ -736,3 +736,42 @@ def test_forward_replays_under_hip_graph_capture():
     torch.cuda.synchronize()
     assert torch.equal(buf.out.view(torch.int16), buf2.out.view(torch.int16))
     assert torch.equal(buf.bitmask, buf2.bitmask)
+
+
+def test_concurrent_streams_and_threads():
+    # two host threads, each with its own stream, buffers and workload, run the
+    # path at the same time; each result must equal its single-stream result
+    import threading
+
+    cases = [SMALL[1][1], SMALL[3][1]]
+    setups, refs = [], []
+    for w in cases:
+        q, k, v, qd, kd, vd, buf = setup(w)
+        F.forward(buf, qd, kd, vd, w.top_p, w.topk_floor, w.aug_budget)
+        torch.cuda.synchronize()
+        refs.append((buf.out.clone(), buf.bitmask.clone()))
+        setups.append((w, qd, kd, vd, buf))
+    errors = []
+
+    def worker(i):
+        try:
+            w, qd, kd, vd, buf = setups[i]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(10):
+                    buf.out.fill_(float("nan"))
+                    F.forward(buf, qd, kd, vd, w.top_p, w.topk_floor, w.aug_budget)
+            s.synchronize()
+        except Exception as e:  # reported below, on the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for (w, qd, kd, vd, buf), (out, bm) in zip(setups, refs):
+        assert torch.equal(buf.out.view(torch.int16), out.view(torch.int16)), w.name
+        assert torch.equal(buf.bitmask, bm), w.name
