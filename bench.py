@@ -226,10 +226,9 @@ def main():
     from adaptive_block_sparse_reorder_amd import fva as F
     from adaptive_block_sparse_reorder_amd.inputs import WORKLOADS, make_qkv
 
+    sched_name = args.sched
     args.sched = {"queue": F.FVA_SCHED_QUEUE, "static": F.FVA_SCHED_STATIC,
-                  "grid": F.FVA_SCHED_GRID, "xcd": F.FVA_SCHED_XCD}[args.sched]
-    sched_name = {v: k for k, v in {"queue": F.FVA_SCHED_QUEUE, "static": F.FVA_SCHED_STATIC,
-                  "grid": F.FVA_SCHED_GRID, "xcd": F.FVA_SCHED_XCD}.items()}[args.sched]
+                  "grid": F.FVA_SCHED_GRID, "xcd": F.FVA_SCHED_XCD}[sched_name]
     F.load_library()
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
