@@ -56,14 +56,27 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
   const int c = threadIdx.x % CPR;
   const int rg = threadIdx.x / CPR;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int r = rg; r < nreal; r += RG) {
+  // all of a thread's rows (at most 128 / RG) are loaded before any is summed,
+  // so the loads are in flight together.  Rows past the block's real tokens
+  // load the last real row (always in bounds) and are not summed, so the sums
+  // are those of the real rows in row order.
+  constexpr int MAXR = 128 / RG;
+  u32x4 v[MAXR];
+#pragma unroll
+  for (int i = 0; i < MAXR; ++i) {
+    const int r = min(rg + i * RG, nreal - 1);
     const int64_t unit = is_k ? (int64_t)(r >> 6) * 64 * CPR + c * 64 + (r & 63)
                               : (int64_t)r * CPR + c;
-    const u32x4 v = *(const u32x4*)(x + unit * 8);
-    acc[0] += bf16_lo(v.x); acc[1] += bf16_hi(v.x);
-    acc[2] += bf16_lo(v.y); acc[3] += bf16_hi(v.y);
-    acc[4] += bf16_lo(v.z); acc[5] += bf16_hi(v.z);
-    acc[6] += bf16_lo(v.w); acc[7] += bf16_hi(v.w);
+    v[i] = __builtin_nontemporal_load((const u32x4*)(x + unit * 8));
+  }
+#pragma unroll
+  for (int i = 0; i < MAXR; ++i) {
+    if (rg + i * RG < nreal) {
+      acc[0] += bf16_lo(v[i].x); acc[1] += bf16_hi(v[i].x);
+      acc[2] += bf16_lo(v[i].y); acc[3] += bf16_hi(v[i].y);
+      acc[4] += bf16_lo(v[i].z); acc[5] += bf16_hi(v[i].z);
+      acc[6] += bf16_lo(v[i].w); acc[7] += bf16_hi(v[i].w);
+    }
   }
   // reduce the row groups of this wave (lanes that share a chunk), then across waves
 #pragma unroll
