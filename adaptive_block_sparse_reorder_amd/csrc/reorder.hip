@@ -72,16 +72,25 @@ __global__ __launch_bounds__(kThreads) void reorder_rows_inv(
   __syncthreads();
   const int cpr = d >> 3;
   const int total = kRows * Hh * cpr;
-  for (int L = threadIdx.x; L < total; L += kThreads) {
-    const int c = L % cpr;
-    const int rh = L / cpr;
-    const int h = rh % Hh;
-    const int rl = rh / Hh;
-    const int64_t n = tok[rl];
-    if (n < 0) continue;
-    const int64_t r = r0 + rl;
-    const u32x4 v = *(const u32x4*)(src + (((int64_t)b * Hh + h) * Npad + r) * d + c * 8);
-    *(u32x4*)(dst + b * sb + n * sn + h * sh + c * 8) = v;
+  // four loads in flight per thread, read non-temporally (read once)
+  for (int L0 = threadIdx.x; L0 < total; L0 += 4 * kThreads) {
+    u32x4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int L = min(L0 + j * kThreads, total - 1);
+      const int c = L % cpr, rh = L / cpr, h = rh % Hh, rl = rh / Hh;
+      v[j] = __builtin_nontemporal_load(
+          (const u32x4*)(src + (((int64_t)b * Hh + h) * Npad + r0 + rl) * d + c * 8));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int L = L0 + j * kThreads;
+      if (L >= total) continue;
+      const int c = L % cpr, rh = L / cpr, h = rh % Hh, rl = rh / Hh;
+      const int64_t n = tok[rl];
+      if (n < 0) continue;
+      *(u32x4*)(dst + b * sb + n * sn + h * sh + c * 8) = v[j];
+    }
   }
 }
 
