@@ -1,6 +1,7 @@
-// Block-sparse flash attention for gfx950 (FVAttn page, section 2: only the
-// selected query-key block pairs are evaluated; section 3.2: work is balanced
-// on the realized per-row workload, here by persistent work queues).
+// Block-sparse flash attention for gfx950 (FVAttn page, section 2: the block
+// mask decides which query-block/key-block pairs are computed; section 3.2:
+// work is balanced on the realized per-row workload, here by persistent work
+// queues).
 //
 // Work item = one query block (BLK rows) of one head, processed by one
 // workgroup of BLK/32 waves; each wave owns 32 queries and walks every

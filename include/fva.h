@@ -11,8 +11,8 @@
  *     key-block importance order (sections 2 and 3.1),
  *   - slack-aware augmentation, here a per-head top-up of further high-score
  *     blocks up to a pair budget (section 3.3),
- *   - block-sparse attention in which only selected query-key block pairs are
- *     evaluated (section 2), run as a persistent kernel over a heaviest-first
+ *   - block-sparse attention computed for the chosen (query block, key block)
+ *     pairs alone (section 2), run as a persistent kernel over a heaviest-first
  *     work queue, the one-GPU counterpart of runtime load balancing
  *     (section 3.2).
  *
@@ -151,9 +151,9 @@ fva_status fva_reorder(const void* src, void* dst, int32_t B, int32_t Hh, int32_
                        const fva_grid* grid, const int64_t strides[3],
                        int32_t direction, int32_t layout, hipStream_t stream);
 
-/* Tile orders for the block organization (section 3.1: blocks are ordered
- * along a Hilbert curve so that spatially adjacent tokens fall into nearby
- * blocks across scales). */
+/* Tile orders for the block organization (section 3.1): tiles may be visited
+ * along a 3-D Hilbert index, which keeps tiles that neighbour each other in
+ * the video grid close together in the block sequence. */
 #define FVA_ORDER_RASTER 0   /* tiles in raster order (what fva_reorder uses)   */
 #define FVA_ORDER_HILBERT 1  /* tiles by their 3-D Hilbert index over (tile
                                 frame, tile row, tile column) on the bounding
@@ -204,8 +204,9 @@ fva_status fva_route(const void* qr, const void* kr, int32_t B, int32_t Hh, int3
  * synchronously on `stream`.  Bit 0: a NaN score was seen.                 */
 fva_status fva_route_flags(const void* ws, uint32_t* flags_out, hipStream_t stream);
 
-/* Block-sparse attention (section 2: only selected query-key block pairs are
- * evaluated).  For each real query token of block i of head (b, h):
+/* Block-sparse attention (section 2: the mask decides which (query block,
+ * key block) pairs are computed).  For each real query token of block i of
+ * head (b, h):
  *   out = sum over the real keys of the selected key blocks of
  *         softmax_k((q . k) * scale) * v_k,
  * computed with bf16 MFMA products, float32 accumulation and an online

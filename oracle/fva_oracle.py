@@ -17,8 +17,9 @@ Steps and the passages they follow (all on the FVAttn page):
   pool                               section 3.1, block similarities from pooled Q/K
   block_scores                       section 2 (importance score per head, q-block,
                                      k-block) and section 3.1 (pooled Q/K)
-  route                              section 2 (Top-p: smallest set whose cumulative
-                                     normalized importance reaches p; Top-k floor)
+  route                              section 2 (Top-p: the shortest importance-ordered
+                                     run of key blocks holding at least a share p of
+                                     the row's normalized scores; Top-k floor)
                                      and section 3.1 (Top-p CDF threshold, Top-k floor)
   head_workload                      section 2 (realized per-head workload = number
                                      of selected block pairs)
@@ -31,8 +32,13 @@ Steps and the passages they follow (all on the FVAttn page):
                                      coefficient), on virtual ranks
   heaviest_first                     section 3.2 (load balancing on realized
                                      workloads), one-GPU work-queue form
-  sparse_attention                   section 2 (only selected query-key block pairs
-                                     are evaluated)
+  load_imbalance / trace_unit_busy /  section 2 (load-imbalance factor: largest
+  cu_imbalance / slot_imbalance      unit load over the mean unit load), with the
+                                     units taken as the GPU's compute units or
+                                     resident workgroup slots and a unit's load
+                                     as the time it spent on work items
+  sparse_attention                   section 2 (attention is computed for the
+                                     chosen query-block/key-block pairs and no others)
   sparse_lse / mask_recall           section 2 (the softmax normalizer over the keys
                                      of the selected blocks); recall as the share of
                                      the full softmax mass those keys hold (reading;
@@ -288,6 +294,71 @@ def sasa_topup(S32: np.ndarray, mask: np.ndarray, budget) -> np.ndarray:
             pick = np.lexsort((fj, fi, -s))[:need]
             m[fi[pick], fj[pick]] = True
     return out
+
+
+def load_imbalance(loads) -> float:
+    """Load-imbalance factor of section 2: the largest unit load divided by the
+    mean load over all R units (idle units count with load 0).  1 means
+    perfectly balanced; R means one unit carries everything."""
+    L = [float(x) for x in loads]
+    if not L:
+        raise ValueError("no units")
+    mean = sum(L) / len(L)
+    if mean <= 0.0:
+        raise ValueError("total load is zero")
+    return max(L) / mean
+
+
+# Attention trace records: 8 uint32 per processed work item,
+#   (row, XCC_ID register, HW_ID register, workgroup id, t0 lo, t0 hi, t1 lo, t1 hi)
+# with t0/t1 the item's start and end on the 100 MHz real-time counter.  The
+# compute unit that ran the item is named by the XCC_ID register's bits 3:0
+# (which XCD) and the HW_ID register's bits 15:8 (CU id bits 11:8, shader array
+# bit 12, shader engine bits 15:13, unique inside one XCD).  The HW_ID bits
+# below 8 (wave, SIMD, pipe) vary inside one CU and are not part of the name.
+
+def _record_fields(rec):
+    r = [int(x) & 0xFFFFFFFF for x in rec]
+    unit = ((r[1] & 0xF) << 8) | ((r[2] >> 8) & 0xFF)
+    t0 = r[4] | (r[5] << 32)
+    t1 = r[6] | (r[7] << 32)
+    if t1 < t0:
+        raise ValueError("record ends before it starts")
+    return unit, t0, t1
+
+
+def trace_unit_busy(records) -> Dict[int, int]:
+    """Busy time of each compute unit seen in the trace: the sum of the
+    durations t1 - t0 of the items it ran (ticks), keyed by (xcc << 8) | cu."""
+    busy: Dict[int, int] = {}
+    for rec in records:
+        unit, t0, t1 = _record_fields(rec)
+        busy[unit] = busy.get(unit, 0) + (t1 - t0)
+    return busy
+
+
+def cu_imbalance(records, n_units: int) -> float:
+    """Per-CU load-imbalance factor of one traced launch: load_imbalance over
+    all n_units compute units of the GPU, a unit's load being its busy time
+    (CUs that ran nothing count with load 0)."""
+    busy = trace_unit_busy(records)
+    if len(busy) > n_units:
+        raise ValueError("more units in the trace than the GPU has")
+    loads = list(busy.values()) + [0] * (n_units - len(busy))
+    return load_imbalance(loads)
+
+
+def slot_imbalance(records, slots: int) -> float:
+    """The same factor over the launch's resident workgroup slots: the slowest
+    slot finishes when the launch does, so the largest slot load is the span
+    max(t1) - min(t0), and the mean slot load is the total item time over the
+    number of slots."""
+    spans = [_record_fields(rec)[1:] for rec in records]
+    span = max(t1 for _, t1 in spans) - min(t0 for t0, _ in spans)
+    total = sum(t1 - t0 for t0, t1 in spans)
+    if total <= 0:
+        raise ValueError("total item time is zero")
+    return span * slots / total
 
 
 def heaviest_first(counts: np.ndarray) -> np.ndarray:

@@ -148,6 +148,29 @@ def test_route_worked_examples():
         assert counts[0, 0, 0] == len(case["selected"])
 
 
+def test_route_margin_worked_examples():
+    # the cut's distance from flipping, worked by hand in the fixture
+    g = _load("route_worked.json")
+    for case in g["cases"]:
+        s = np.array(case["s"], dtype=np.float32)[None, None, None, :]
+        _, _, margin = O.route(s, case["p"], case["k"])
+        if case["margin"] is None:
+            assert margin[0, 0, 0] == np.inf, case
+        else:
+            assert margin[0, 0, 0] == pytest.approx(case["margin"], abs=2e-10), case
+
+
+def test_head_workload_hand_worked():
+    # W_h counts the selected (query block, key block) pairs of a head;
+    # B = 2, Hh = 2, nB = 3 masks written out by hand
+    m = np.zeros((2, 2, 3, 3), dtype=bool)
+    m[0, 0] = np.eye(3, dtype=bool)               # 3 pairs, one per row
+    m[0, 1] = True                                # all 9 pairs
+    m[1, 1, 0, :] = True                          # head (1,0) stays empty
+    m[1, 1, 2, 1] = True                          # 3 + 1 pairs
+    assert O.head_workload(m).tolist() == [[3, 9], [0, 4]]
+
+
 def _brute_min_card(s, p):
     """Smallest subset size whose softmax mass reaches p (math.fsum, all subsets)."""
     n = len(s)
@@ -268,6 +291,70 @@ def test_sasa_disabled_and_saturated():
     mask, _, _ = O.route(S, 0.5, 1)
     assert np.array_equal(O.sasa_topup(S, mask, 0), mask)
     assert O.sasa_topup(S, mask, 10 ** 6).all()
+
+
+def test_sasa_budget_cap_hand_worked():
+    # contiguous heads [10, 1 | 2, 1] on 2 ranks: loads 11 and 3, so rank 1 has
+    # slack 8; alpha 1 gives it 8 extra pairs, 4 per head: wanted 6 and 5
+    roh = [0, 0, 1, 1]
+    assert O.sasa_budget([10, 1, 2, 1], roh, 2, 1.0, 1000).tolist() == [10, 1, 6, 5]
+    # a cap below W_h + share binds: both heads stop at 5
+    assert O.sasa_budget([10, 1, 2, 1], roh, 2, 1.0, 5).tolist() == [10, 1, 5, 5]
+    # heads [10, 1 | 7, 1]: loads 11 and 8, slack 3 -> shares 2 (lower id) and 1
+    assert O.sasa_budget([10, 1, 7, 1], roh, 2, 1.0, 1000).tolist() == [10, 1, 9, 2]
+    # a cap below W_h never lowers a head's budget under its own workload
+    assert O.sasa_budget([10, 1, 7, 1], roh, 2, 1.0, 5).tolist() == [10, 1, 7, 2]
+    # alpha 0.5: floor(1.5) = 1 extra pair, to the lower head id
+    assert O.sasa_budget([10, 1, 7, 1], roh, 2, 0.5, 1000).tolist() == [10, 1, 8, 1]
+
+
+def test_sasa_budget_invariants_when_the_cap_binds():
+    rng = np.random.default_rng(9)
+    for _ in range(200):
+        R = int(rng.integers(1, 6))
+        W = [int(x) for x in rng.integers(0, 200, size=R * int(rng.integers(1, 4)))]
+        roh = [int(x) for x in rng.integers(0, R, size=len(W))]
+        alpha = float(rng.choice([0.25, 0.5, 1.0]))
+        cap = int(rng.integers(0, 250))
+        hb = O.sasa_budget(W, roh, R, alpha, cap)
+        loose = O.sasa_budget(W, roh, R, alpha, 10 ** 9)
+        for h in range(len(W)):
+            assert hb[h] >= W[h]                           # never below the workload
+            assert hb[h] <= max(cap, W[h])                 # never above the cap
+            assert hb[h] == max(W[h], min(loose[h], cap))  # the cap only clips
+
+
+# ----------------------------------------------------------------- imbalance
+
+def _rec(row, xcc, hw, t0, t1):
+    return [row, xcc, hw, row, t0 & 0xFFFFFFFF, t0 >> 32, t1 & 0xFFFFFFFF, t1 >> 32]
+
+
+def test_imbalance_hand_worked_trace():
+    # four items on three compute units, times straddling a 32-bit wrap of the
+    # counter's low word.  Unit A = XCD 0, CU 3: two items of 30 and 25 ticks
+    # (different wave/SIMD bits in HW_ID, junk above bit 3 of XCC_ID); unit B =
+    # XCD 1, CU 3: 15 ticks; unit C = XCD 0, CU 3 of shader engine 1 (HW_ID
+    # bit 13): 45 ticks.
+    base = (1 << 32) - 60
+    recs = [_rec(0, 0x30, 0x0325, base, base + 30),
+            _rec(1, 0x00, 0x0311, base + 35, base + 60),
+            _rec(2, 0x01, 0x0300, base + 2, base + 17),
+            _rec(3, 0x00, 0x2300, base + 10, base + 55)]
+    assert O.trace_unit_busy(recs) == {0x003: 55, 0x103: 15, 0x023: 45}
+    # 4 CUs, one idle: loads 55, 15, 45, 0 -> mean 28.75, factor 55 / 28.75
+    assert O.cu_imbalance(recs, 4) == pytest.approx(55 / 28.75, rel=1e-15)
+    assert O.cu_imbalance(recs, 3) == pytest.approx(55 / (115 / 3), rel=1e-15)
+    # 4 slots: the span (60 ticks) over the mean slot load (115 / 4)
+    assert O.slot_imbalance(recs, 4) == pytest.approx(60 * 4 / 115, rel=1e-15)
+
+
+def test_load_imbalance_rank_form():
+    # section 2's factor on ranks: W = [10, 9, 1, 1] on 2 ranks carries 19 and 2
+    L = O.rank_loads([10, 9, 1, 1], O.contiguous_placement(4, 2), 2)
+    assert O.load_imbalance(L) == pytest.approx(19 / 10.5, rel=1e-15)
+    assert O.load_imbalance([7, 7, 7]) == 1.0
+    assert O.load_imbalance([12, 0, 0]) == 3.0
 
 
 # ----------------------------------------------------------------- queue

@@ -81,6 +81,42 @@ MUTANTS = [
      "np.exp(np.asarray(lse_selected, np.float64) - np.asarray(lse_all, np.float64))",
      "np.exp(np.asarray(lse_all, np.float64) - np.asarray(lse_selected, np.float64))",
      ["test_recall_equals_dense_mass_on_selected_blocks"]),
+    ("margin not normalized by Z", "margin[r] = m / Z", "margin[r] = m",
+     ["test_route_margin_worked_examples"]),
+    ("margin ignores the n*-1 side", "m = min(m, abs(C[nstar - 2] - target))", "m = m",
+     ["test_route_margin_worked_examples"]),
+    ("head workload always zero",
+     "mask.reshape(mask.shape[0], mask.shape[1], -1).sum(axis=-1).astype(np.int64)",
+     "mask.reshape(mask.shape[0], mask.shape[1], -1).sum(axis=-1).astype(np.int64) * 0",
+     ["test_head_workload_hand_worked"]),
+    ("head workload counts rows, not pairs",
+     "mask.reshape(mask.shape[0], mask.shape[1], -1).sum(axis=-1).astype(np.int64)",
+     "mask.any(axis=-1).sum(axis=-1).astype(np.int64)",
+     ["test_head_workload_hand_worked"]),
+    ("sasa budget cap ignored",
+     "out[h] = min(max(want, int(W[h])), max(head_cap, int(W[h])))",
+     "out[h] = max(want, int(W[h]))",
+     ["test_sasa_budget_cap_hand_worked", "test_sasa_budget_invariants_when_the_cap_binds"]),
+    ("sasa budget cap lowers a head below its workload",
+     "out[h] = min(max(want, int(W[h])), max(head_cap, int(W[h])))",
+     "out[h] = min(want, head_cap)",
+     ["test_sasa_budget_cap_hand_worked", "test_sasa_budget_invariants_when_the_cap_binds"]),
+    ("sasa remainder to the highest head ids", "want = int(W[h]) + q + (1 if k < rem else 0)",
+     "want = int(W[h]) + q + (1 if k >= len(hs) - rem else 0)",
+     ["test_sasa_budget_cap_hand_worked"]),
+    ("CU named without shader-engine bits", "((r[2] >> 8) & 0xFF)", "((r[2] >> 8) & 0xF)",
+     ["test_imbalance_hand_worked_trace"]),
+    ("CU named with wave and SIMD bits", "((r[2] >> 8) & 0xFF)", "(r[2] & 0xFFFF)",
+     ["test_imbalance_hand_worked_trace"]),
+    ("XCC_ID not masked", "unit = ((r[1] & 0xF) << 8)", "unit = ((r[1]) << 8)",
+     ["test_imbalance_hand_worked_trace"]),
+    ("CU mean over the units seen only",
+     "loads = list(busy.values()) + [0] * (n_units - len(busy))", "loads = list(busy.values())",
+     ["test_imbalance_hand_worked_trace"]),
+    ("imbalance as max over min", "return max(L) / mean", "return max(L) / min(L)",
+     ["test_load_imbalance_rank_form"]),
+    ("slot imbalance without the slot count", "return span * slots / total",
+     "return span / total", ["test_imbalance_hand_worked_trace"]),
 ]
 
 
