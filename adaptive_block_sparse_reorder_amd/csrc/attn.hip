@@ -81,18 +81,15 @@ __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t rs, uint32_t vo
 // every read is conflict-free and its address is one per-lane base plus an
 // immediate offset.
 
-// Attention workspace: [0,256) counters and per-XCD offsets, then per-head
-// bases, then the XCD-ordered row list.
+// Attention workspace: [0,256) counters and per-XCD offsets, then the
+// XCD-ordered row list.
 struct AttnWs {
   static constexpr int kQueueCtr = 0;      // int: global queue counter
   static constexpr int kXcdCtr = 16;       // int[8]: per-XCD counters
   static constexpr int kXcdOff = 32;       // int[9]: per-XCD offsets into xq
-  __host__ __device__ static size_t head_base_off() { return 256; }
-  __host__ __device__ static size_t xq_off(int64_t nheads) {
-    return 256 + ((nheads * 4 + 255) & ~(int64_t)255);
-  }
-  __host__ __device__ static size_t bytes(int64_t nheads, int64_t rows) {
-    return xq_off(nheads) + ((rows * 4 + 255) & ~(int64_t)255);
+  __host__ __device__ static size_t xq_off() { return 256; }
+  __host__ __device__ static size_t bytes(int64_t rows) {
+    return xq_off() + ((rows * 4 + 255) & ~(int64_t)255);
   }
 };
 
@@ -444,17 +441,21 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_
 
 __global__ void zero_counter(int32_t* ws) { ws[AttnWs::kQueueCtr] = 0; }
 
-// XCD plan, step 1 (one workgroup): order heads by W_h descending (ties by
-// head id), assign them greedily to the least-loaded XCD, and lay the XCD
-// row lists out contiguously: XCD x owns [off[x], off[x+1]) and its heads
-// follow in assignment order, nB rows each.
+// XCD plan (one workgroup): order heads by W_h descending (ties by head id),
+// assign them greedily to the least-loaded XCD (longest processing time
+// first), lay the XCD row lists out contiguously (XCD x owns [off[x],
+// off[x+1]) and its heads follow in assignment order, nB rows each), and
+// write every head's rows in query-block order at its place.  Neighbouring
+// query blocks select mostly the same key blocks, so the workgroups resident
+// on one XCD stream shared K/V tiles through that XCD's L2; balance comes
+// from the head placement and stealing.
 constexpr int kPlanThreads = 256;
 
-__global__ __launch_bounds__(kPlanThreads) void xcd_assign_kernel(const int32_t* head_count,
-                                                                  int nheads, int nB, int32_t* ws) {
+__global__ __launch_bounds__(kPlanThreads) void xcd_plan_kernel(const int32_t* head_count,
+                                                                int nheads, int nB, int32_t* ws) {
   __shared__ uint64_t keys[kMaxXcdHeads];
-  __shared__ int16_t hx[kMaxXcdHeads];
-  __shared__ int32_t hpos[kMaxXcdHeads];
+  __shared__ int32_t hbase[kMaxXcdHeads];
+  __shared__ int32_t s_off[NXCD];
   int P = 1;
   while (P < nheads) P <<= 1;
   for (int h = threadIdx.x; h < P; h += kPlanThreads)
@@ -472,17 +473,18 @@ __global__ __launch_bounds__(kPlanThreads) void xcd_assign_kernel(const int32_t*
   if (threadIdx.x == 0) {
     int64_t load[NXCD] = {0, 0, 0, 0, 0, 0, 0, 0};
     int nh[NXCD] = {0, 0, 0, 0, 0, 0, 0, 0};
+    // hbase[h] <- (xcd, position within the xcd), then the row offset
     for (int r = 0; r < nheads; ++r) {
       const int h = (int)(uint32_t)keys[r];
       int best = 0;
       for (int x = 1; x < NXCD; ++x)
         if (load[x] < load[best]) best = x;
       load[best] += head_count[h];
-      hx[h] = (int16_t)best;
-      hpos[h] = nh[best]++;
+      hbase[h] = best | (nh[best]++ << 3);
     }
     int off = 0;
     for (int x = 0; x < NXCD; ++x) {
+      s_off[x] = off;
       ws[AttnWs::kXcdOff + x] = off;
       ws[AttnWs::kXcdCtr + x] = 0;
       off += nh[x] * nB;
@@ -490,21 +492,15 @@ __global__ __launch_bounds__(kPlanThreads) void xcd_assign_kernel(const int32_t*
     ws[AttnWs::kXcdOff + NXCD] = off;
   }
   __syncthreads();
-  int32_t* base = ws + AttnWs::head_base_off() / 4;
   for (int h = threadIdx.x; h < nheads; h += kPlanThreads)
-    base[h] = ws[AttnWs::kXcdOff + hx[h]] + hpos[h] * nB;
-}
-
-// XCD plan, step 2 (one workgroup per head): the head's rows in query-block
-// order at its base.  Neighbouring query blocks select mostly the same key
-// blocks, so the workgroups resident on one XCD stream shared K/V tiles
-// through that XCD's L2; balance comes from the head placement and stealing.
-__global__ __launch_bounds__(kPlanThreads) void xcd_fill_kernel(int nB, int32_t* ws,
-                                                                int64_t nheads) {
-  const int64_t h = blockIdx.x;
-  const int32_t base = ws[AttnWs::head_base_off() / 4 + h];
-  int32_t* xq = ws + AttnWs::xq_off(nheads) / 4;
-  for (int i = threadIdx.x; i < nB; i += kPlanThreads) xq[base + i] = (int32_t)(h * nB + i);
+    hbase[h] = s_off[hbase[h] & 7] + (hbase[h] >> 3) * nB;
+  __syncthreads();
+  int32_t* xq = ws + AttnWs::xq_off() / 4;
+  const int64_t rows = (int64_t)nheads * nB;
+  for (int64_t t = threadIdx.x; t < rows; t += kPlanThreads) {
+    const int h = (int)(t / nB);
+    xq[hbase[h] + (t - (int64_t)h * nB)] = (int32_t)t;
+  }
 }
 
 constexpr int kQT = 1;  // 32-query tiles per wave in the launched kernels
@@ -527,21 +523,27 @@ fva_status launch_t(const Problem& p, AttnArgs a, int flags, bool dense, hipStre
       NT, 0);
   if (e != hipSuccess) return hip_fail(e, "occupancy query");
   if (per_cu < 1) per_cu = 1;
-  const int64_t persist = std::min<int64_t>(p.rows, (int64_t)cus * per_cu);
+  const int64_t slots = (int64_t)cus * per_cu;
+  const int64_t persist = std::min<int64_t>(p.rows, slots);
 #define FVA_LAUNCH(SCH, TR, GRIDN)                                                         \
   hipLaunchKernelGGL((attn_kernel<D, BLK, kQT, SCH, false, TR>), dim3((unsigned)(GRIDN)), dim3(NT), \
                      0, s, a)
-  if (sched == FVA_SCHED_QUEUE) {
+  // When every item fits in one wave of resident workgroups, each persistent
+  // workgroup of the queue and XCD schedules would run exactly one item: one
+  // plain launch over the heaviest-first queue does the same work without the
+  // counter reset or the XCD plan.
+  if ((sched == FVA_SCHED_QUEUE || sched == FVA_SCHED_XCD) && p.rows <= slots) {
+    if (trace) FVA_LAUNCH(FVA_SCHED_GRID, true, p.rows);
+    else FVA_LAUNCH(FVA_SCHED_GRID, false, p.rows);
+  } else if (sched == FVA_SCHED_QUEUE) {
     hipLaunchKernelGGL(zero_counter, dim3(1), dim3(1), 0, s, a.ws);
     if (trace) FVA_LAUNCH(FVA_SCHED_QUEUE, true, persist);
     else FVA_LAUNCH(FVA_SCHED_QUEUE, false, persist);
   } else if (sched == FVA_SCHED_XCD) {
     const int nheads = p.B * p.Hh;
-    hipLaunchKernelGGL(xcd_assign_kernel, dim3(1), dim3(kPlanThreads), 0, s, a.head_count, nheads,
+    hipLaunchKernelGGL(xcd_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a.head_count, nheads,
                        p.nB, a.ws);
-    hipLaunchKernelGGL(xcd_fill_kernel, dim3(nheads), dim3(kPlanThreads), 0, s, p.nB, a.ws,
-                       (int64_t)nheads);
-    a.queue = a.ws + AttnWs::xq_off(nheads) / 4;
+    a.queue = a.ws + AttnWs::xq_off() / 4;
     if (trace) FVA_LAUNCH(FVA_SCHED_XCD, true, persist);
     else FVA_LAUNCH(FVA_SCHED_XCD, false, persist);
   } else if (sched == FVA_SCHED_STATIC) {
@@ -557,7 +559,7 @@ fva_status launch_t(const Problem& p, AttnArgs a, int flags, bool dense, hipStre
 
 }  // namespace
 
-size_t attn_ws_bytes(const Problem& p) { return AttnWs::bytes((int64_t)p.B * p.Hh, p.rows); }
+size_t attn_ws_bytes(const Problem& p) { return AttnWs::bytes(p.rows); }
 
 fva_status launch_attn(const Problem& p, const void* qr, const void* kr, const void* vt,
                        void* out, const fva_mask* m, float scale, int flags, void* ws,

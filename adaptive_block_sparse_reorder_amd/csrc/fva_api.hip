@@ -132,7 +132,7 @@ fva_status fva_sizes(const fva_grid* grid, int32_t B, int32_t Hh, int32_t d, fva
 }
 
 fva_status fva_reorder_ex(const void* src, void* dst, int32_t B, int32_t Hh, int32_t d,
-                          const fva_grid* grid, const void* table, const int64_t strides[3],
+                          const fva_grid* grid, void* table, const int64_t strides[3],
                           int32_t direction, int32_t layout, hipStream_t stream) {
   Problem p;
   fva_status st = make_problem(grid, B, Hh, d, &p);
@@ -152,7 +152,8 @@ fva_status fva_reorder_ex(const void* src, void* dst, int32_t B, int32_t Hh, int
   if (strides[2] < d) return fail(FVA_ERR_INVALID_ARG, "head stride smaller than d");
   if (table && tile_count(p) > kMaxTiles)
     return fail(FVA_ERR_UNSUPPORTED, "%lld tiles exceed %d", (long long)tile_count(p), kMaxTiles);
-  return launch_reorder(p, src, dst, strides, direction, layout, (const int32_t*)table, stream);
+  if (table && !aligned16(table)) return fail(FVA_ERR_INVALID_ARG, "table must be 16-byte aligned");
+  return launch_reorder(p, src, dst, strides, direction, layout, (int32_t*)table, stream);
 }
 
 fva_status fva_reorder(const void* src, void* dst, int32_t B, int32_t Hh, int32_t d,
@@ -185,6 +186,15 @@ fva_status fva_tile_order(const fva_grid* grid, int32_t order, void* table, size
   Problem p;
   make_problem(grid, 1, 1, 64, &p);
   return launch_tile_order(p, order, (int32_t*)table, stream);
+}
+
+fva_status fva_tile_table_status(const void* table, int32_t* status_out, hipStream_t stream) {
+  if (!table || !status_out) return fail(FVA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(table)) return fail(FVA_ERR_INVALID_ARG, "table must be 16-byte aligned");
+  hipError_t e = hipMemcpyAsync(status_out, (const int32_t*)table + 2, sizeof(int32_t),
+                                hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  return hip_fail(e, "tile table status copy");
 }
 
 fva_status fva_route(const void* qr, const void* kr, int32_t B, int32_t Hh, int32_t d,

@@ -15,6 +15,75 @@
 namespace fva {
 namespace {
 
+// Reordered position r (< N) -> source token index.  Tokens inside a tile
+// are always visited in raster order (t, y, x).  Tiles are visited either in
+// raster order (closed form: every tile-frame slab covers whole frames and
+// every tile row inside a slab covers whole rows, so the tile containing r
+// follows from three divisions) or in the order of a tile table (tile_id[k],
+// start[k] = first reordered position of the k-th tile), found by binary
+// search.  A table lookup is bounded: it returns -1 (and raises the table's
+// status word) when the table's header names another grid or an entry does
+// not describe a tile of this grid, and it never indexes past the table.
+struct BlockOrder {
+  int32_t T, H, W, bt, bh, bw;
+  int32_t* table;          // null: raster tile order
+  int32_t ntiles;          // tiles of this grid
+  __device__ __forceinline__ int64_t src_token(int64_t r) const {
+    if (table) return src_token_table(r);
+    const int64_t HW = (int64_t)H * W;
+    const int64_t slab = (int64_t)bt * HW;
+    const int32_t tt = (int32_t)(r / slab);
+    int64_t r1 = r - (int64_t)tt * slab;
+    const int32_t st = min(bt, T - tt * bt);
+    const int64_t rowband = (int64_t)st * bh * W;
+    const int32_t ty = (int32_t)(r1 / rowband);
+    int64_t r2 = r1 - (int64_t)ty * rowband;
+    const int32_t sy = min(bh, H - ty * bh);
+    const int32_t tilesz = st * sy * bw;
+    const int32_t tx = (int32_t)(r2 / tilesz);
+    const int32_t r3 = (int32_t)(r2 - (int64_t)tx * tilesz);
+    const int32_t sx = min(bw, W - tx * bw);
+    const int32_t t = r3 / (sy * sx);
+    const int32_t rem = r3 - t * (sy * sx);
+    const int32_t y = rem / sx;
+    const int32_t x = rem - y * sx;
+    return ((int64_t)(tt * bt + t) * H + (ty * bh + y)) * W + (tx * bw + x);
+  }
+  __device__ __forceinline__ bool header_matches() const {
+    const int32_t* h = table;
+    return h[0] == ntiles && h[3] == T && h[4] == H && h[5] == W && h[6] == bt && h[7] == bh &&
+           h[8] == bw;
+  }
+  __device__ int64_t src_token_table(int64_t r) const {
+    if (!header_matches()) return bad();
+    const int32_t* tile_id = table + kTableHeaderWords;
+    const int32_t* start = tile_id + ntiles;
+    int lo = 0, hi = ntiles;  // start[lo] <= r < start[hi] for a well-formed table
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((int64_t)start[mid] <= r) lo = mid;
+      else hi = mid;
+    }
+    const int32_t nty = (H + bh - 1) / bh, ntx = (W + bw - 1) / bw;
+    const int32_t id = tile_id[lo];
+    if (id < 0 || id >= ntiles) return bad();
+    const int32_t tt = id / (nty * ntx), ty = (id / ntx) % nty, tx = id % ntx;
+    const int32_t st = min(bt, T - tt * bt), sy = min(bh, H - ty * bh), sx = min(bw, W - tx * bw);
+    const int64_t o64 = r - (int64_t)start[lo];
+    if (o64 < 0 || o64 >= (int64_t)st * sy * sx) return bad();
+    const int32_t o = (int32_t)o64;
+    const int32_t t = o / (sy * sx);
+    const int32_t rem = o - t * (sy * sx);
+    const int32_t y = rem / sx;
+    const int32_t x = rem - y * sx;
+    return ((int64_t)(tt * bt + t) * H + (ty * bh + y)) * W + (tx * bw + x);
+  }
+  __device__ int64_t bad() const {
+    atomicOr(table + 2, 1);
+    return -1;
+  }
+};
+
 constexpr int kRows = 8;
 constexpr int kThreads = 256;
 
@@ -229,7 +298,7 @@ __global__ __launch_bounds__(kOrderThreads) void tile_order_kernel(BlockOrder g,
       }
       __syncthreads();
     }
-  int32_t* tile_id = table + 4;
+  int32_t* tile_id = table + kTableHeaderWords;
   int32_t* start = tile_id + ntiles;
   // each thread owns a contiguous run of tiles; exclusive scan of their sizes
   const int per = (ntiles + kOrderThreads - 1) / kOrderThreads;
@@ -260,10 +329,9 @@ __global__ __launch_bounds__(kOrderThreads) void tile_order_kernel(BlockOrder g,
   }
   if (threadIdx.x == 0) {
     start[ntiles] = (int32_t)N;
-    table[0] = ntiles;
-    table[1] = order;
-    table[2] = 0;
-    table[3] = 0;
+    const int32_t hdr[kTableHeaderWords] = {ntiles, order, 0, g.T, g.H, g.W, g.bt, g.bh, g.bw,
+                                            0, 0, 0};
+    for (int w = 0; w < kTableHeaderWords; ++w) table[w] = hdr[w];
   }
 }
 
@@ -274,20 +342,14 @@ int64_t tile_count(const Problem& p) {
 }
 
 fva_status launch_tile_order(const Problem& p, int order, int32_t* table, hipStream_t s) {
-  BlockOrder g{p.T, p.H, p.W, p.bt, p.bh, p.bw, nullptr, nullptr, 0};
+  BlockOrder g{p.T, p.H, p.W, p.bt, p.bh, p.bw, nullptr, 0};
   hipLaunchKernelGGL(tile_order_kernel, dim3(1), dim3(kOrderThreads), 0, s, g, order, p.N, table);
   return hip_fail(hipGetLastError(), "tile order launch");
 }
 
 fva_status launch_reorder(const Problem& p, const void* src, void* dst, const int64_t st[3],
-                          int direction, int layout, const int32_t* table, hipStream_t s) {
-  BlockOrder bo{p.T, p.H, p.W, p.bt, p.bh, p.bw, nullptr, nullptr, 0};
-  if (table) {
-    const int64_t nt = tile_count(p);
-    bo.tile_id = table + 4;
-    bo.start = table + 4 + nt;
-    bo.ntiles = (int32_t)nt;
-  }
+                          int direction, int layout, int32_t* table, hipStream_t s) {
+  BlockOrder bo{p.T, p.H, p.W, p.bt, p.bh, p.bw, table, (int32_t)tile_count(p)};
   const uint16_t* in = (const uint16_t*)src;
   uint16_t* out = (uint16_t*)dst;
   if (direction == FVA_FORWARD && layout == FVA_LAYOUT_ROWS) {

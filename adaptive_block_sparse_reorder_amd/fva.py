@@ -107,6 +107,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                    ctypes.POINTER(ctypes.c_int64), I32, I32, P]
     lib.fva_tile_order_bytes.argtypes = [ctypes.POINTER(fva_grid), ctypes.POINTER(ctypes.c_size_t)]
     lib.fva_tile_order.argtypes = [ctypes.POINTER(fva_grid), I32, P, SZ, P]
+    lib.fva_tile_table_status.argtypes = [P, ctypes.POINTER(ctypes.c_int32), P]
     PI32 = ctypes.POINTER(ctypes.c_int32)
     PI64 = ctypes.POINTER(ctypes.c_int64)
     lib.fva_rlb_plan.argtypes = [PI32, I32, I32, I32, PI32, PI32, PI32,
@@ -116,7 +117,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                               ctypes.POINTER(fva_mask), P, SZ, P]
     for fn in ("fva_sizes", "fva_reorder", "fva_route", "fva_route_flags", "fva_sparse_attn",
                "fva_dense_attn", "fva_rlb_plan", "fva_sasa_budget", "fva_topup",
-               "fva_reorder_ex", "fva_tile_order_bytes", "fva_tile_order"):
+               "fva_reorder_ex", "fva_tile_order_bytes", "fva_tile_order",
+               "fva_tile_table_status"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.fva_status_string.argtypes = [ctypes.c_int]
     lib.fva_status_string.restype = ctypes.c_char_p
@@ -193,6 +195,17 @@ def fva_tile_order(grid: fva_grid, order: int, table, table_bytes: int, stream=N
     lib = load_library()
     _check(lib.fva_tile_order(ctypes.byref(grid), order, _ptr(table), table_bytes,
                               _stream(stream)), "fva_tile_order")
+
+
+def fva_tile_table_status(table, stream=None) -> int:
+    lib = load_library()
+    v = ctypes.c_int32(0)
+    _check(lib.fva_tile_table_status(_ptr(table), ctypes.byref(v), _stream(stream)),
+           "fva_tile_table_status")
+    return int(v.value)
+
+
+TILE_TABLE_HEADER_WORDS = 12
 
 
 def tile_table(grid: fva_grid, order: int = FVA_ORDER_HILBERT, device="cuda", stream=None):

@@ -42,6 +42,10 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip dense comparator and schedule traces (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--configs", default="tiny,480p,hetero,long720p",
+                    help="other workloads measured after the headline one (comma list, "
+                         "'' for none): per-stage ms, attention TFLOP/s, dense comparator, "
+                         "imbalance per schedule, top-up ms")
     ap.add_argument("--sched", default="xcd", choices=["queue", "static", "grid", "xcd"])
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB "
@@ -73,12 +77,15 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def lambda_cu(trace_u32, rows, slots=512):
+def lambda_cu(trace_u32, rows, slots=512, n_units=256):
     """Imbalance of one traced launch: the load-imbalance factor of the FVAttn
-    page (papers.paperslantern.ai/papers/2607.16190, section 2: maximum over
-    mean realized load), taken over CUs and over workgroup slots of one GPU.
+    page (papers.paperslantern.ai/papers/2607.16190, section 2: largest unit
+    load over the mean unit load), taken over the GPU's CUs and over its
+    resident workgroup slots.
 
-    lambda_cu:   per-CU busy time (sum of its item durations), max/mean over CUs.
+    lambda_cu:   per-CU busy time (sum of its item durations), max over the
+                 mean of all n_units CUs (a CU that ran nothing counts as 0).
+                 A CU is named by XCC_ID bits 3:0 and HW_ID bits 15:8.
     lambda_slot: critical path over mean slot load, span * slots / sum of item
                  durations, with slots = resident workgroups (2 per CU here).  A
                  CU hosting one long and one short workgroup looks balanced to
@@ -90,13 +97,14 @@ def lambda_cu(trace_u32, rows, slots=512):
     dur = (t1 - t0).astype(np.float64)
     xcc = tr[:, 1] & 0xF
     hw = tr[:, 2]
-    cu_key = (xcc.astype(np.int64) << 16) | ((hw >> 8) & 0xFF).astype(np.int64)
+    cu_key = (xcc.astype(np.int64) << 8) | ((hw >> 8) & 0xFF).astype(np.int64)
     keys, inv = np.unique(cu_key, return_inverse=True)
     busy = np.bincount(inv, weights=dur)
+    n = max(int(n_units), len(keys))
     span = float(t1.max() - t0.min())
-    return dict(lambda_cu=float(busy.max() / busy.mean()),
+    return dict(lambda_cu=float(busy.max() / (busy.sum() / n)),
                 lambda_slot=float(span * slots / dur.sum()), cus=int(len(keys)),
-                busy_max_ms=float(busy.max()) / 1e5, busy_mean_ms=float(busy.mean()) / 1e5,
+                busy_max_ms=float(busy.max()) / 1e5, busy_mean_ms=float(busy.sum() / n) / 1e5,
                 span_ms=span / 1e5)
 
 
@@ -149,6 +157,129 @@ def cpu_baseline(w, q, k, v, seconds):
                    f"{w.B * w.Hh * w.nB} rows {t2 - t1:.1f} s (not in value)"),
         "route_density": float(r["head_count"].sum() / (w.B * w.Hh * w.nB ** 2)),
     }
+
+
+def config_block(name, sched_flag, cus, slots, reps=3):
+    """The whole path on another workload, timed stage by stage with HIP events
+    on the launch stream (median of `reps` passes after two warm passes), with
+    the dense comparator, the per-CU / per-slot imbalance of every schedule
+    (traced launches), the realized density and, when the workload tops heads
+    up to a pair budget, the top-up's own time."""
+    import numpy as np
+    import torch
+    from adaptive_block_sparse_reorder_amd import fva as F
+    from adaptive_block_sparse_reorder_amd.inputs import WORKLOADS, make_qkv
+
+    w = WORKLOADS[name]
+    log(f"config {name}: generating inputs")
+    q, k, v = make_qkv(w)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    del q, k, v
+    buf = F.alloc_buffers(w.grid, w.block, w.B, w.Hh, w.d, trace=True)
+    g, m = buf.grid, buf.mask()
+    stream = torch.cuda.current_stream()
+    prm = F.fva_route_params(w.top_p, w.topk_floor, w.aug_budget, 0.0, 0)
+
+    def event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def reorders():
+        for x, dst, lay in ((qd, buf.qr, F.FVA_LAYOUT_ROWS), (kd, buf.kr, F.FVA_LAYOUT_K64),
+                            (vd, buf.vt, F.FVA_LAYOUT_V64)):
+            F.fva_reorder(x, dst, w.B, w.Hh, w.d, g, F.token_strides(x), F.FVA_FORWARD, lay)
+
+    def attn(flags, trace=None):
+        F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, g, m, 0.0, flags,
+                          buf.attn_ws, buf.sizes.attn_ws_bytes, trace)
+
+    log(f"config {name}: timing the path")
+    for _ in range(2):
+        F.forward(buf, qd, kd, vd, w.top_p, w.topk_floor, w.aug_budget, attn_flags=sched_flag)
+    torch.cuda.synchronize()
+    laps = []
+    for _ in range(reps):
+        e = [event()]
+        reorders()
+        e.append(event())
+        F.fva_route(buf.qr, buf.kr, w.B, w.Hh, w.d, g, prm, m, buf.route_ws,
+                    buf.sizes.route_ws_bytes, 0)
+        e.append(event())
+        attn(sched_flag)
+        e.append(event())
+        F.fva_reorder(buf.orr, buf.out, w.B, w.Hh, w.d, g, F.token_strides(buf.out),
+                      F.FVA_INVERSE)
+        e.append(event())
+        laps.append(e)
+    torch.cuda.synchronize()
+    ms = np.median([[a.elapsed_time(b) for a, b in zip(e[:-1], e[1:])] for e in laps], axis=0)
+    nnz = int(buf.row_count.sum().item())
+    ex = F.executed_flops(nnz, w.d, w.BLK)
+    de = F.dense_equiv_flops(w.N, w.d, w.Hh, w.B)
+    dens = buf.head_count.cpu().numpy().astype(np.float64) / (w.nB ** 2)
+    for _ in range(2):
+        F.fva_dense_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, g)
+    dl = []
+    for _ in range(reps):
+        a = event()
+        F.fva_dense_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, g)
+        dl.append((a, event()))
+    torch.cuda.synchronize()
+    ms_dense = float(np.median([a.elapsed_time(b) for a, b in dl]))
+    lam = {}
+    for sname, fl in (("static", F.FVA_SCHED_STATIC), ("grid", F.FVA_SCHED_GRID),
+                      ("queue", F.FVA_SCHED_QUEUE), ("xcd", F.FVA_SCHED_XCD)):
+        buf.trace.zero_()
+        attn(fl | F.FVA_TRACE, buf.trace)
+        torch.cuda.synchronize()
+        lc = lambda_cu(buf.trace.cpu().numpy().view(np.uint32), int(buf.sizes.rows), slots, cus)
+        lam[sname] = {"lambda_cu": round(lc["lambda_cu"], 4),
+                      "lambda_slot": round(lc["lambda_slot"], 4), "cus": lc["cus"]}
+    out = {
+        "workload": (f"B={w.B} heads={w.Hh} d={w.d} grid={w.grid[0]}x{w.grid[1]}x{w.grid[2]} "
+                     f"({w.N} tokens, {w.nB} blocks of {w.BLK}) block={w.block[0]}x{w.block[1]}x"
+                     f"{w.block[2]} top_p={w.top_p} topk_floor={w.topk_floor} "
+                     f"aug_budget={w.aug_budget}"),
+        "rows": int(buf.sizes.rows),
+        "density": {"mean": round(float(dens.mean()), 4), "min": round(float(dens.min()), 4),
+                    "max": round(float(dens.max()), 4)},
+        "reorder_qkv_ms": round(float(ms[0]), 4),
+        "route_ms": round(float(ms[1]), 4),
+        "sparse_attn_ms": round(float(ms[2]), 4),
+        "unreorder_ms": round(float(ms[3]), 4),
+        "step_ms": round(float(ms.sum()), 4),
+        "executed_tflop": round(ex / 1e12, 4),
+        "executed_tflops": round(ex / (ms[2] * 1e-3) / 1e12, 2),
+        "frac": round(ex / (ms[2] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "dense_equiv_tflops": round(de / (ms[2] * 1e-3) / 1e12, 2),
+        "dense_ms": round(ms_dense, 4),
+        "speedup_vs_dense": round(ms_dense / float(ms[2]), 4),
+        "imbalance": lam,
+    }
+    if w.aug_budget > 0:
+        # the same top-up as inside the routing call, on its own: route
+        # without a budget, then raise every head to the budget
+        prm0 = F.fva_route_params(w.top_p, w.topk_floor, 0, 0.0, 0)
+        budgets = torch.full((w.B * w.Hh,), w.aug_budget, dtype=torch.int64, device="cuda")
+        tl = []
+        for _ in range(reps):
+            F.fva_route(buf.qr, buf.kr, w.B, w.Hh, w.d, g, prm0, m, buf.route_ws,
+                        buf.sizes.route_ws_bytes, 0)
+            a = event()
+            F.fva_topup(w.B, w.Hh, w.d, g, budgets, m, buf.route_ws, buf.sizes.route_ws_bytes)
+            tl.append((a, event()))
+        torch.cuda.synchronize()
+        out["topup_ms"] = round(float(np.median([a.elapsed_time(b) for a, b in tl])), 4)
+        F.fva_route(buf.qr, buf.kr, w.B, w.Hh, w.d, g, prm0, m, buf.route_ws,
+                    buf.sizes.route_ws_bytes, 0)
+        torch.cuda.synchronize()
+        out["topup_pairs_added"] = nnz - int(buf.row_count.sum().item())
+    del buf, qd, kd, vd
+    torch.cuda.empty_cache()
+    log(f"config {name}: attention {out['sparse_attn_ms']} ms, "
+        f"{out['executed_tflops']} TFLOP/s, dense {out['dense_ms']} ms")
+    return out
 
 
 def recall_stats(lse_sel, lse_all):
@@ -332,7 +463,8 @@ def main():
                   "topp_raster": recall_stats(lse_sel, lse_all)}
         # per-CU and per-slot imbalance under each schedule (2 resident
         # workgroups per CU: 64 KB of LDS each)
-        slots = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        slots = 2 * cus
         lam = {}
         for name, fl in (("static", F.FVA_SCHED_STATIC), ("grid", F.FVA_SCHED_GRID),
                          ("queue", F.FVA_SCHED_QUEUE), ("xcd", F.FVA_SCHED_XCD)):
@@ -341,7 +473,7 @@ def main():
                               fl | F.FVA_TRACE, buf.attn_ws, buf.sizes.attn_ws_bytes, buf.trace)
             torch.cuda.synchronize()
             lam[name] = lambda_cu(buf.trace.cpu().numpy().view(np.uint32), int(buf.sizes.rows),
-                                  slots)
+                                  slots, cus)
         extras["lambda_cu"] = lam
 
     if not args.no_extras:
@@ -403,7 +535,8 @@ def main():
                               fl | F.FVA_TRACE, buf.attn_ws, buf.sizes.attn_ws_bytes, buf.trace)
             k1.record(stream)
             torch.cuda.synchronize()
-            lc = lambda_cu(buf.trace.cpu().numpy().view(np.uint32), int(buf.sizes.rows), slots)
+            lc = lambda_cu(buf.trace.cpu().numpy().view(np.uint32), int(buf.sizes.rows), slots,
+                           cus)
             fk[name] = {"lambda_cu": round(lc["lambda_cu"], 4),
                         "lambda_slot": round(lc["lambda_slot"], 4),
                         "attn_ms_traced": round(k0.elapsed_time(k1), 3)}
@@ -478,6 +611,11 @@ def main():
         "rank_max_after": int(max(rank_after)),
         "density_after": round(float(buf.head_count.sum().item()) / (w.Hh * w.B * w.nB ** 2), 4),
     }
+
+    if not args.no_extras and args.configs:
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        extras["configs"] = {c: config_block(c, args.sched, cus, 2 * cus)
+                             for c in args.configs.split(",") if c and c != w.name}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -163,19 +163,31 @@ fva_status fva_reorder(const void* src, void* dst, int32_t B, int32_t Hh, int32_
 fva_status fva_tile_order_bytes(const fva_grid* grid, size_t* bytes);
 
 /* Writes the tile table of `order` for `grid` into the DEVICE buffer `table`
- * (fva_tile_order_bytes() bytes): {ntiles, order, 0, 0} then the raster id of
- * the k-th tile, then the first reordered position of the k-th tile
- * (ntiles + 1 entries, the last = N).  Tokens inside a tile stay in raster
- * order.                                                                    */
+ * (fva_tile_order_bytes() bytes, 16-byte aligned): a header of 12 int32
+ * {ntiles, order, status = 0, T, H, W, bt, bh, bw, 0, 0, 0}, then the raster
+ * id of the k-th tile (ntiles entries), then the first reordered position of
+ * the k-th tile (ntiles + 1 entries, the last = N).  Tokens inside a tile stay
+ * in raster order.                                                          */
 fva_status fva_tile_order(const fva_grid* grid, int32_t order, void* table, size_t table_bytes,
                           hipStream_t stream);
 
 /* fva_reorder with the tile order taken from a table written by
- * fva_tile_order (DEVICE pointer); table = NULL is raster order.  All other
- * arguments and layouts are as for fva_reorder.                             */
+ * fva_tile_order for the SAME grid and block shape (DEVICE pointer, 16-byte
+ * aligned); table = NULL is raster order.  All other arguments and layouts
+ * are as for fva_reorder.  The kernels compare the table's header with
+ * `grid` and check every entry they use before indexing with it: a table of
+ * another grid, or a damaged one, never makes them read outside the table or
+ * the source.  Positions they cannot place are written as zero (forward) or
+ * not written (inverse), and the table's status word (header word 2) is set
+ * to 1; read it with fva_tile_table_status.                                 */
 fva_status fva_reorder_ex(const void* src, void* dst, int32_t B, int32_t Hh, int32_t d,
-                          const fva_grid* grid, const void* table, const int64_t strides[3],
+                          const fva_grid* grid, void* table, const int64_t strides[3],
                           int32_t direction, int32_t layout, hipStream_t stream);
+
+/* Copies a tile table's status word (0 = every lookup so far was consistent,
+ * 1 = a reorder found the table does not belong to its grid) to *status_out
+ * (host), synchronously on `stream`.                                        */
+fva_status fva_tile_table_status(const void* table, int32_t* status_out, hipStream_t stream);
 
 /* Sparse-routing frontend (sections 2 and 3.1; top-up section 3.3).
  * qr: `rows` bf16, kr: `k64` bf16.  For every row (b, h, i):

@@ -37,7 +37,7 @@ def test_sizes_match_workloads(lib, name, N, Npad, nB, words):
     assert (s.N, s.Npad, s.nB, s.words, s.BLK) == (N, Npad, nB, words, w.BLK)
     assert s.rows == w.B * w.Hh * nB
     assert s.trace_bytes == 32 * s.rows
-    assert s.attn_ws_bytes >= 256 + 4 * s.rows + 4 * w.Hh
+    assert s.attn_ws_bytes >= 256 + 4 * s.rows
     # route workspace: status word + pooled q, k (float32) + per-head thresholds
     assert s.route_ws_bytes >= 256 + 2 * 4 * s.rows * w.d + 8 * w.Hh
 
@@ -108,12 +108,13 @@ def test_validation_errors_before_launch(lib):
 
 
 def test_tile_table_sizes_and_limits(lib):
-    # the documented layout: {ntiles, order, 0, 0}, ntiles raster ids, ntiles + 1 starts
+    # the documented layout: a 12-word header {ntiles, order, status, T, H, W,
+    # bt, bh, bw, 0, 0, 0}, ntiles raster ids, ntiles + 1 starts
     g = F.make_grid((3, 13, 19), (1, 8, 8))          # 3 x 2 x 3 = 18 tiles, clipped in y and x
     nbytes = ctypes.c_size_t(0)
     assert lib.fva_tile_order_bytes(ctypes.byref(g), ctypes.byref(nbytes)) == F.FVA_OK
     need = nbytes.value
-    assert need == 16 + 4 * 18 + 4 * 19
+    assert need == 48 + 4 * 18 + 4 * 19
     assert lib.fva_tile_order_bytes(ctypes.byref(g), None) == F.FVA_ERR_INVALID_ARG
     # heavy clipping: 15000 frames of a 1 x 17 strip with 1x8x16 tiles give 30000
     # tiles but only 1993 blocks, past the tile table's 8192-tile capacity
@@ -133,3 +134,10 @@ def test_tile_table_sizes_and_limits(lib):
     assert lib.fva_tile_order(ctypes.byref(g), 7, 256, 1 << 20, None) == F.FVA_ERR_INVALID_ARG
     assert lib.fva_tile_order(ctypes.byref(g), F.FVA_ORDER_HILBERT, 264, 1 << 20, None) == \
         F.FVA_ERR_INVALID_ARG
+    # a misaligned table is refused by the reorder and the status read too
+    assert lib.fva_reorder_ex(256, 512, 1, 1, 64, ctypes.byref(g), 1028, st, F.FVA_FORWARD,
+                              F.FVA_LAYOUT_ROWS, None) == F.FVA_ERR_INVALID_ARG
+    out = ctypes.c_int32(0)
+    assert lib.fva_tile_table_status(None, ctypes.byref(out), None) == F.FVA_ERR_INVALID_ARG
+    assert lib.fva_tile_table_status(1028, ctypes.byref(out), None) == F.FVA_ERR_INVALID_ARG
+    assert lib.fva_tile_table_status(1024, None, None) == F.FVA_ERR_INVALID_ARG

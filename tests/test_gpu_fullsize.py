@@ -103,13 +103,28 @@ def run_case(w, n_random=12):
         routed = r["mask_routed"].reshape(w.B * w.Hh, -1).sum(-1)
         assert np.all(hc == np.maximum(routed, np.minimum(w.aug_budget, w.nB * w.nB)))
 
-    print(f"[{w.name}] attention (XCD schedule) on sampled query blocks", flush=True)
+    print(f"[{w.name}] attention under every schedule, output prefilled with NaN", flush=True)
+    outs = {}
+    for fl in (F.FVA_SCHED_QUEUE, F.FVA_SCHED_STATIC, F.FVA_SCHED_GRID):
+        buf.orr.fill_(float("nan"))
+        F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, buf.grid, buf.mask(),
+                          0.0, fl, buf.attn_ws, buf.sizes.attn_ws_bytes)
+        torch.cuda.synchronize()
+        outs[fl] = buf.orr.clone()
     nq = w.B * w.Hh * w.N
     lse_s = torch.full((nq,), float("nan"), dtype=torch.float32, device="cuda")
     lse_d = torch.full((nq,), float("nan"), dtype=torch.float32, device="cuda")
+    buf.orr.fill_(float("nan"))
     F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, buf.grid, buf.mask(),
                       0.0, F.FVA_SCHED_XCD, buf.attn_ws, buf.sizes.attn_ws_bytes, lse=lse_s)
     torch.cuda.synchronize()
+    # every real row written (finite), every pad row zero, every schedule bit-identical
+    assert bool(torch.isfinite(buf.orr[:, :, :w.N]).all())
+    assert not bool(buf.orr[:, :, w.N:].any())
+    for fl, o in outs.items():
+        assert torch.equal(o.view(torch.int16), buf.orr.view(torch.int16)), fl
+    del outs
+    assert bool(torch.isfinite(lse_s).all()) or w.topk_floor == 0
     rows = set()
     counts = r["counts"].reshape(-1)
     rows.add(int(np.argmax(counts)))
