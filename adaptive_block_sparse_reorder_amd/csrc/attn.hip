@@ -33,6 +33,7 @@
 // most key blocks, so their K/V stream through that XCD's L2 once), and a
 // workgroup whose XCD runs dry steals from the other XCDs' lists.
 #include <algorithm>
+#include <mutex>
 
 #include "fva_internal.hpp"
 
@@ -557,9 +558,34 @@ fva_status launch_t(const Problem& p, AttnArgs a, int flags, bool dense, hipStre
   return hip_fail(hipGetLastError(), "sparse attention launch");
 }
 
+// Attention workspace for callers that cannot allocate: every device that
+// loads the library holds its own copy of this array until the process ends.
+// Host code uses only the device address that hipGetSymbolAddress returns
+// for it (per device), never the array's name.
+static __device__ __align__(256) char scratch[FVA_NOALLOC_ATTN_WS_MAX];
+
 }  // namespace
 
 size_t attn_ws_bytes(const Problem& p) { return AttnWs::bytes(p.rows); }
+
+fva_status noalloc_attn_ws(void** out) {
+  static std::mutex mu;
+  static void* ptrs[64] = {nullptr};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "current device");
+  if (dev < 0 || dev >= 64) return fail(FVA_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "scratch symbol address");
+    if (!p) return fail(FVA_ERR_HIP, "scratch symbol address is null");
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return FVA_OK;
+}
 
 fva_status launch_attn(const Problem& p, const void* qr, const void* kr, const void* vt,
                        void* out, const fva_mask* m, float scale, int flags, void* ws,

@@ -258,12 +258,11 @@ static fva_status attn_common(const void* qr, const void* kr, const void* vt, vo
   return FVA_OK;
 }
 
-fva_status fva_sparse_attn(const void* qr, const void* kr, const void* vt, void* out, int32_t B,
-                           int32_t Hh, int32_t d, const fva_grid* grid, const fva_mask* mask,
-                           float scale, int32_t flags, void* ws, size_t ws_bytes, void* trace,
-                           void* lse, hipStream_t stream) {
-  Problem p;
-  fva_status st = attn_common(qr, kr, vt, out, B, Hh, d, grid, &p);
+static fva_status sparse_attn_checked(const void* qr, const void* kr, const void* vt, void* out,
+                                      int32_t B, int32_t Hh, int32_t d, const fva_grid* grid,
+                                      const fva_mask* mask, float scale, int32_t flags,
+                                      Problem* p) {
+  fva_status st = attn_common(qr, kr, vt, out, B, Hh, d, grid, p);
   if (st != FVA_OK) return st;
   st = check_mask(mask, false);
   if (st != FVA_OK) return st;
@@ -271,16 +270,52 @@ fva_status fva_sparse_attn(const void* qr, const void* kr, const void* vt, void*
   if (flags & ~(0x3 | FVA_TRACE)) return fail(FVA_ERR_INVALID_ARG, "flags 0x%x", flags);
   if (sched == FVA_SCHED_XCD && (int64_t)B * Hh > kMaxXcdHeads)
     return fail(FVA_ERR_UNSUPPORTED, "FVA_SCHED_XCD supports at most %d heads", kMaxXcdHeads);
+  return FVA_OK;
+}
+
+static fva_status sparse_attn_launch(const Problem& p, const void* qr, const void* kr,
+                                     const void* vt, void* out, const fva_mask* mask, float scale,
+                                     int32_t flags, void* ws, void* trace, void* lse,
+                                     hipStream_t stream) {
+  if ((flags & FVA_TRACE) && !trace) return fail(FVA_ERR_INVALID_ARG, "FVA_TRACE needs a trace buffer");
+  if (!(flags & FVA_TRACE)) trace = nullptr;
+  if (((uintptr_t)lse & 3u) != 0) return fail(FVA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (!(scale > 0.f)) scale = 1.0f / sqrtf((float)p.d);
+  return launch_attn(p, qr, kr, vt, out, mask, scale, flags, ws, trace, lse, false, stream);
+}
+
+fva_status fva_sparse_attn(const void* qr, const void* kr, const void* vt, void* out, int32_t B,
+                           int32_t Hh, int32_t d, const fva_grid* grid, const fva_mask* mask,
+                           float scale, int32_t flags, void* ws, size_t ws_bytes, void* trace,
+                           void* lse, hipStream_t stream) {
+  Problem p;
+  fva_status st = sparse_attn_checked(qr, kr, vt, out, B, Hh, d, grid, mask, scale, flags, &p);
+  if (st != FVA_OK) return st;
   const size_t need = attn_ws_bytes(p);
   if (!ws || ws_bytes < need)
     return fail(FVA_ERR_WORKSPACE, "attention workspace needs %zu bytes, got %zu", need,
                 ws ? ws_bytes : (size_t)0);
   if (((uintptr_t)ws & 255u) != 0) return fail(FVA_ERR_WORKSPACE, "workspace not 256-byte aligned");
-  if ((flags & FVA_TRACE) && !trace) return fail(FVA_ERR_INVALID_ARG, "FVA_TRACE needs a trace buffer");
-  if (!(flags & FVA_TRACE)) trace = nullptr;
-  if (((uintptr_t)lse & 3u) != 0) return fail(FVA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-  if (!(scale > 0.f)) scale = 1.0f / sqrtf((float)d);
-  return launch_attn(p, qr, kr, vt, out, mask, scale, flags, ws, trace, lse, false, stream);
+  return sparse_attn_launch(p, qr, kr, vt, out, mask, scale, flags, ws, trace, lse, stream);
+}
+
+fva_status fva_sparse_attn_noalloc(const void* qr, const void* kr, const void* vt, void* out,
+                                   int32_t B, int32_t Hh, int32_t d, const fva_grid* grid,
+                                   const fva_mask* mask, float scale, int32_t flags, void* trace,
+                                   void* lse, hipStream_t stream) {
+  Problem p;
+  fva_status st = sparse_attn_checked(qr, kr, vt, out, B, Hh, d, grid, mask, scale, flags, &p);
+  if (st != FVA_OK) return st;
+  const size_t need = attn_ws_bytes(p);
+  if (need > (size_t)FVA_NOALLOC_ATTN_WS_MAX)
+    return fail(FVA_ERR_UNSUPPORTED,
+                "%lld rows need %zu bytes of attention workspace; the library's own holds %d "
+                "(pass a workspace to fva_sparse_attn instead)",
+                (long long)p.rows, need, FVA_NOALLOC_ATTN_WS_MAX);
+  void* ws = nullptr;
+  st = noalloc_attn_ws(&ws);
+  if (st != FVA_OK) return st;
+  return sparse_attn_launch(p, qr, kr, vt, out, mask, scale, flags, ws, trace, lse, stream);
 }
 
 fva_status fva_dense_attn(const void* qr, const void* kr, const void* vt, void* out, int32_t B,

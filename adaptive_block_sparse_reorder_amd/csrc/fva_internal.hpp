@@ -45,6 +45,9 @@ struct RouteWs {
 RouteWs route_ws_layout(const Problem& p);
 // Bytes of the attention workspace (scheduler counters and XCD row lists).
 size_t attn_ws_bytes(const Problem& p);
+// Device address of the library's own attention workspace on the current
+// device (FVA_NOALLOC_ATTN_WS_MAX bytes; looked up once per device).
+fva_status noalloc_attn_ws(void** out);
 constexpr int kMaxXcdHeads = 4096;
 
 // Kernel launchers (each returns FVA_OK or FVA_ERR_HIP).

@@ -103,6 +103,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fva_sparse_attn.argtypes = [P, P, P, P, I32, I32, I32, ctypes.POINTER(fva_grid),
                                     ctypes.POINTER(fva_mask), F, I32, P, SZ, P, P, P]
     lib.fva_dense_attn.argtypes = [P, P, P, P, I32, I32, I32, ctypes.POINTER(fva_grid), F, P, P]
+    lib.fva_sparse_attn_noalloc.argtypes = [P, P, P, P, I32, I32, I32, ctypes.POINTER(fva_grid),
+                                            ctypes.POINTER(fva_mask), F, I32, P, P, P]
     lib.fva_reorder_ex.argtypes = [P, P, I32, I32, I32, ctypes.POINTER(fva_grid), P,
                                    ctypes.POINTER(ctypes.c_int64), I32, I32, P]
     lib.fva_tile_order_bytes.argtypes = [ctypes.POINTER(fva_grid), ctypes.POINTER(ctypes.c_size_t)]
@@ -118,7 +120,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for fn in ("fva_sizes", "fva_reorder", "fva_route", "fva_route_flags", "fva_sparse_attn",
                "fva_dense_attn", "fva_rlb_plan", "fva_sasa_budget", "fva_topup",
                "fva_reorder_ex", "fva_tile_order_bytes", "fva_tile_order",
-               "fva_tile_table_status"):
+               "fva_tile_table_status", "fva_sparse_attn_noalloc"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.fva_status_string.argtypes = [ctypes.c_int]
     lib.fva_status_string.restype = ctypes.c_char_p
@@ -242,6 +244,21 @@ def fva_sparse_attn(qr, kr, vt, out, B: int, Hh: int, d: int, grid: fva_grid, ma
                                ctypes.byref(grid), ctypes.byref(mask), scale, flags, _ptr(ws),
                                ws_bytes, _ptr(trace), _ptr(lse), _stream(stream)),
            "fva_sparse_attn")
+
+
+FVA_NOALLOC_ATTN_WS_MAX = 1 << 20
+
+
+def fva_sparse_attn_noalloc(qr, kr, vt, out, B: int, Hh: int, d: int, grid: fva_grid,
+                            mask: fva_mask, scale: float = 0.0, flags: int = FVA_SCHED_QUEUE,
+                            trace=None, stream=None, lse=None):
+    """fva_sparse_attn with the library's own static workspace (no caller
+    workspace, no allocation)."""
+    lib = load_library()
+    _check(lib.fva_sparse_attn_noalloc(_ptr(qr), _ptr(kr), _ptr(vt), _ptr(out), B, Hh, d,
+                                       ctypes.byref(grid), ctypes.byref(mask), scale, flags,
+                                       _ptr(trace), _ptr(lse), _stream(stream)),
+           "fva_sparse_attn_noalloc")
 
 
 def fva_dense_attn(qr, kr, vt, out, B: int, Hh: int, d: int, grid: fva_grid, scale: float = 0.0,

@@ -244,6 +244,23 @@ fva_status fva_sparse_attn(const void* qr, const void* kr, const void* vt, void*
                            void* ws, size_t ws_bytes, void* trace, void* lse,
                            hipStream_t stream);
 
+/* fva_sparse_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and results, with the attention workspace taken from a
+ * static array of FVA_NOALLOC_ATTN_WS_MAX bytes that the library holds on
+ * each device until the process ends, instead of a caller buffer.  The call
+ * itself allocates nothing.  Problems whose workspace would exceed that
+ * (more than about 262 000 rows, fva_sizes().attn_ws_bytes) return
+ * FVA_ERR_UNSUPPORTED before any launch.  Every call on one device shares
+ * that device's array: calls that overlap in time on one device (two streams,
+ * two threads) race and must be serialized by the caller.  The kernels
+ * initialize whatever they need in it, so no clearing is required.          */
+#define FVA_NOALLOC_ATTN_WS_MAX (1 << 20)
+fva_status fva_sparse_attn_noalloc(const void* qr, const void* kr, const void* vt, void* out,
+                                   int32_t B, int32_t Hh, int32_t d, const fva_grid* grid,
+                                   const fva_mask* mask, float scale, int32_t flags,
+                                   void* trace, void* lse, hipStream_t stream);
+
 /* Dense attention over every key block with the same core: the comparator
  * for the sparse kernel.  Same layouts, output and lse conventions as above
  * (lse then sums over all real keys).                                      */
