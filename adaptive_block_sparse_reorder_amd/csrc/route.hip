@@ -142,22 +142,6 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qb
 
 // ------------------------------------------------------------------ block helpers
 
-// Inclusive scan of doubles across a 256-thread block (4 waves).
-__device__ double block_incl_scan_f64(double v, double* wsum) {
-  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
-  if (lane == 63) wsum[wave] = v;
-  __syncthreads();
-  double base = 0.0;
-  for (int w = 0; w < wave; ++w) base += wsum[w];
-  __syncthreads();
-  return base + v;
-}
-
 template <int NT>
 __device__ int block_sum_i32(int v, int* red) {
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
@@ -188,56 +172,6 @@ __device__ void bitonic_sort(K* keys, int P) {
   }
 }
 
-// Ascending bitonic sort of P = 256*E 64-bit keys, E per thread in
-// registers: thread t holds positions t*E .. t*E+E-1, before and after.  A
-// compare-exchange partner closer than E is in the same thread, one closer
-// than 64*E is in the same wave (lane exchange), and only farther partners go
-// through LDS, with a barrier.
-template <int E>
-__device__ void bitonic_sort_regs(uint64_t (&v)[E], uint64_t* xch) {
-  constexpr int P = 256 * E;
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int k = 2; k <= P; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j < E) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          if (e & j) continue;
-          const bool up = ((t * E + e) & k) == 0;
-          const uint64_t x = v[e], y = v[e | j];
-          if ((x > y) == up) { v[e] = y; v[e | j] = x; }
-        }
-      } else {
-        uint64_t o[E];
-        if (j < 64 * E) {
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v[e], j / E, 64);
-            const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v[e] >> 32), j / E, 64);
-            o[e] = ((uint64_t)hi << 32) | lo;
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < E; ++e) xch[t * E + e] = v[e];
-          __syncthreads();
-#pragma unroll
-          for (int e = 0; e < E; ++e) o[e] = xch[(t * E + e) ^ j];
-          __syncthreads();
-        }
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int i = t * E + e;
-          const bool keep_min = ((i & j) == 0) == ((i & k) == 0);
-          const bool less = v[e] < o[e];
-          v[e] = (keep_min == less) ? v[e] : o[e];
-        }
-      }
-    }
-  }
-}
-
 // Writes bitmask words, and the ascending column list, of one row from the
 // LDS bitmask `bits` (words entries).  Returns nothing; col_idx gets popcount
 // entries.  Must be called by all threads of the block.
@@ -263,86 +197,179 @@ __device__ void emit_row(const uint32_t* bits, int words, uint32_t* bm_out, int1
 }
 
 // ------------------------------------------------------------------ route
-// One 256-thread workgroup per row; P = padded sort length (power of two).
+// One wave per row, E = ceil(nB/64) scores per lane (lane l holds key blocks
+// l, l+64, l+128, ...).  No sort: the selected set is a prefix of the
+// importance order (score descending, key block ascending), so it is the set
+// of keys at or above a threshold key.  The 43-bit priority key is
+// order_key(score) << 11 | (2047 - j): larger means earlier in the order, and
+// it is unique within a row.
+//   Top-p: with e_j = exp(s_j - max) in float64, Z = sum e_j and target
+//   p*Z, the cut key is the largest key x whose tail mass S(x) = sum of e_j
+//   over keys >= x reaches the target; it is found bit by bit from the top
+//   (43 steps), each S(x) a wave sum in a fixed butterfly order.  Adding
+//   terms never lowers a rounded sum, so S is monotone in x exactly as
+//   computed and the search is exact for it.
+//   Top-k floor: the largest key with at least k keys at or above it, by the
+//   same search on ballot counts.
+// The kept set is every key at or above the lower of the two thresholds.
+// Each lane's 64-bit ballot per stride is two bitmask words directly, and
+// ballot prefix counts place the ascending column list.
 constexpr int kRouteThreads = 256;
+constexpr int kRouteRowsPerBlock = kRouteThreads / 64;
 constexpr int kMaxNB = 2048;
+constexpr int kKeyBits = 43;
+
+// Sum of a double over the wave, the same bits in every lane.  Each step adds
+// a partner lane's value with DPP or a lane swap (no LDS traffic): mirror
+// inside 8 lanes, swap pairs of 2, swap neighbours, mirror inside 16, swap
+// rows of 16, swap halves of 32.  Every step pairs lanes symmetrically and
+// addition commutes, so all lanes hold identical partial sums after each step.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)u, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double swap_add_f64(double v, bool rows32) {
+  const uint64_t u = __double_as_longlong(v);
+  uint32_t lo0, lo1, hi0, hi1;
+  if (rows32) {
+    const auto l = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+    lo0 = l[0]; lo1 = l[1]; hi0 = h[0]; hi1 = h[1];
+  } else {
+    const auto l = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+    lo0 = l[0]; lo1 = l[1]; hi0 = h[0]; hi1 = h[1];
+  }
+  return __longlong_as_double((long long)(((uint64_t)hi0 << 32) | lo0)) +
+         __longlong_as_double((long long)(((uint64_t)hi1 << 32) | lo1));
+}
+constexpr int kDppHalfMirror = 0x141, kDppRowMirror = 0x140;
+constexpr int kDppQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_f64<kDppHalfMirror>(v);
+  v += dpp_f64<kDppQuadSwap2>(v);
+  v += dpp_f64<kDppQuadSwap1>(v);
+  v += dpp_f64<kDppRowMirror>(v);
+  v = swap_add_f64(v, false);
+  return swap_add_f64(v, true);
+}
 
 template <int E>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
-    const float* __restrict__ S, int nB, int words, float top_p, int topk,
+    const float* __restrict__ S, int nB, int words, int64_t rows, float top_p, int topk,
     uint32_t* __restrict__ bitmask, int32_t* __restrict__ row_count,
     int16_t* __restrict__ col_idx, int32_t* __restrict__ head_count, uint32_t* flags) {
-  __shared__ uint64_t xch[256 * E];
-  __shared__ uint32_t bits[kMaxNB / 32];
-  __shared__ double wsum[4];
-  __shared__ int red[4];
-  __shared__ int wpre[kMaxNB / 32];
-  __shared__ double s_max;
-  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRouteRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;  // whole wave: no barriers below
   const int64_t bh = row / nB;
   const float* s = S + row * nB;
-  const int t0 = threadIdx.x * E;  // this thread's sort positions t0 .. t0+E-1
-  int nan_seen = 0;
-  uint64_t v[E];
+  uint64_t key[E];
+  float sv[E];
+  bool nan_seen = false;
+  float mx = -INFINITY;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int j = t0 + e;
-    uint64_t key = ~0ull;
+    const int j = lane + 64 * e;
+    key[e] = 0;
+    sv[e] = -INFINITY;
     if (j < nB) {
       const float x = s[j];
       nan_seen |= (x != x);
-      key = ((uint64_t)(~order_key(x)) << 32) | (uint32_t)j;
+      sv[e] = x;
+      key[e] = ((uint64_t)order_key(x) << 11) | (uint64_t)(2047 - j);
+      mx = fmaxf(mx, x);
     }
-    v[e] = key;
   }
-  for (int w = threadIdx.x; w < words; w += kRouteThreads) bits[w] = 0u;
-  if (nan_seen) atomicOr(flags, 1u);
-  bitonic_sort_regs<E>(v, xch);
-  if (threadIdx.x == 0) s_max = (double)order_key_inv(~(uint32_t)(v[0] >> 32));
-  __syncthreads();
+  if (__builtin_amdgcn_ballot_w64(nan_seen) && lane == 0) atomicOr(flags, 1u);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
 
-  // float64 softmax mass accumulated in importance order
-  int nstar;
+  // count of keys >= x over the row (wave-uniform)
+  auto count_ge = [&](uint64_t x) -> int {
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key[e] >= x));
+    return c;
+  };
+
+  // Top-p threshold (all keys when p >= 1, none when p <= 0)
+  uint64_t thr;
   if (top_p >= 1.0f) {
-    nstar = nB;
+    thr = 1;
   } else if (top_p <= 0.0f) {
-    nstar = 0;
+    thr = ~0ull;
   } else {
-    const double m = s_max;
+    const double m = (double)mx;
     double ev[E];
-    double local = 0.0;
+    double part = 0.0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      double x = 0.0;
-      if (t0 + e < nB) x = exp((double)order_key_inv(~(uint32_t)(v[e] >> 32)) - m);
-      ev[e] = x;
-      local += x;
+      ev[e] = key[e] != 0 ? exp((double)sv[e] - m) : 0.0;
+      part += ev[e];
     }
-    const double incl = block_incl_scan_f64(local, wsum);
-    __shared__ double Zs;
-    if (threadIdx.x == kRouteThreads - 1) Zs = incl;
-    __syncthreads();
-    const double target = (double)top_p * Zs;
-    double c = incl - local;
-    int below = 0;
+    const double target = (double)top_p * wave_sum_f64(part);
+    auto search = [&](uint64_t x, int hi_bit, int lo_bit) {
+      for (int b = hi_bit; b >= lo_bit; --b) {
+        const uint64_t c = x | (1ull << b);
+        double t = 0.0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) t += key[e] >= c ? ev[e] : 0.0;
+        if (wave_sum_f64(t) >= target) x = c;
+      }
+      return x;
+    };
+    // the score bits first; the index bits only matter when several keys
+    // share the boundary score, otherwise the cut key is that one key
+    uint64_t x = search(0, kKeyBits - 1, 11);
+    int ties = 0;
+    uint64_t only = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      c += ev[e];
-      if (t0 + e < nB && c < target) ++below;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(key[e] != 0 && (key[e] >> 11) == (x >> 11));
+      ties += __builtin_popcountll(bal);
+      if (bal) {
+        const int l = __builtin_ctzll(bal);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(key[e] >> 32), l);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key[e], l);
+        only = ((uint64_t)hi << 32) | lo;
+      }
     }
-    nstar = min(nB, block_sum_i32<kRouteThreads>(below, red) + 1);
+    thr = ties == 1 ? only : search(x, 10, 0);
   }
-  const int n = min(nB, max(nstar, topk));
+  // Top-k floor: lower the threshold to the k-th key when the cut kept fewer
+  if (topk > 0 && count_ge(thr) < topk) {
+    if (topk >= nB) {
+      thr = 1;
+    } else {
+      uint64_t x = 0;
+      for (int b = kKeyBits - 1; b >= 0; --b) {
+        const uint64_t c = x | (1ull << b);
+        if (count_ge(c) >= topk) x = c;
+      }
+      thr = x;
+    }
+  }
+
+  // bitmask words, ascending column list, counts
+  uint32_t* bm = bitmask + row * words;
+  int16_t* ci = col_idx + row * nB;
+  const uint64_t below = (1ull << lane) - 1ull;
+  int n = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    if (t0 + e < n) {
-      const uint32_t j = (uint32_t)v[e];
-      atomicOr(&bits[j >> 5], 1u << (j & 31));
-    }
+    if (64 * e >= nB) break;
+    const bool sel = key[e] != 0 && key[e] >= thr;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(sel);
+    if (lane < 2 && 2 * e + lane < words) bm[2 * e + lane] = (uint32_t)(bal >> (32 * lane));
+    if (sel) ci[n + __builtin_popcountll(bal & below)] = (int16_t)(lane + 64 * e);
+    n += __builtin_popcountll(bal);
   }
-  __syncthreads();
-  emit_row<kRouteThreads>(bits, words, bitmask + row * words, col_idx + row * nB, wpre);
-  if (threadIdx.x == 0) {
+  if (lane == 0) {
     row_count[row] = n;
     atomicAdd(&head_count[bh], n);
   }
@@ -633,15 +660,21 @@ fva_status launch_route(const Problem& p, const void* qr, const void* kr,
       hipLaunchKernelGGL(score_kernel<64>, sg, dim3(256), 0, s, qbar, kbar, m.scores, p.nB,
                          scale);
   }
-  // sort length: the power of two >= nB, at least one key per thread
-#define FVA_ROUTE(E)                                                                         \
-  hipLaunchKernelGGL(route_kernel<E>, dim3((unsigned)p.rows), dim3(kRouteThreads), 0, s, m.scores, \
-                     p.nB, p.words, prm.top_p, prm.topk_floor, m.bitmask, m.row_count,        \
-                     m.col_idx, m.head_count, wflags)
-  if (p.nB <= 256) FVA_ROUTE(1);
-  else if (p.nB <= 512) FVA_ROUTE(2);
-  else if (p.nB <= 1024) FVA_ROUTE(4);
-  else FVA_ROUTE(8);
+  // scores per lane: ceil(nB / 64), rounded up to an instantiated width
+#define FVA_ROUTE(E)                                                                           \
+  hipLaunchKernelGGL(route_kernel<E>, dim3((unsigned)((p.rows + kRouteRowsPerBlock - 1) /      \
+                                                      kRouteRowsPerBlock)),                    \
+                     dim3(kRouteThreads), 0, s, m.scores, p.nB, p.words, p.rows, prm.top_p,     \
+                     prm.topk_floor, m.bitmask, m.row_count, m.col_idx, m.head_count, wflags)
+  const int per_lane = (p.nB + 63) / 64;
+  if (per_lane <= 2) FVA_ROUTE(2);
+  else if (per_lane <= 4) FVA_ROUTE(4);
+  else if (per_lane <= 8) FVA_ROUTE(8);
+  else if (per_lane <= 10) FVA_ROUTE(10);
+  else if (per_lane <= 12) FVA_ROUTE(12);
+  else if (per_lane <= 16) FVA_ROUTE(16);
+  else if (per_lane <= 24) FVA_ROUTE(24);
+  else FVA_ROUTE(32);
 #undef FVA_ROUTE
   if (prm.aug_budget > 0) launch_topup_kernels(p, m, ws, (int64_t)prm.aug_budget, nullptr, s);
   launch_queue(p, m, ws, s);
