@@ -32,6 +32,9 @@ CFLAGS = [
 ]
 
 SOURCES = ["fva_api.hip", "reorder.hip", "route.hip", "attn.hip", "rlb_host.cpp"]
+# measurement kernels for the benchmark, in a library of their own
+PROBE_SOURCES = ["probe.hip"]
+PROBE_LIB = os.path.join(PKG, "libfva_probe.so")
 
 
 def _compile(src: str) -> str:
@@ -43,19 +46,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, (os.cpu_count() or 4)))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    jobs = min(len(srcs), max(1, (os.cpu_count() or 4)))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

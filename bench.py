@@ -47,6 +47,8 @@ def parse():
                          "'' for none): per-stage ms, attention TFLOP/s, dense comparator, "
                          "imbalance per schedule, top-up ms")
     ap.add_argument("--sched", default="xcd", choices=["queue", "static", "grid", "xcd"])
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="run the matrix-core probe even with --no-extras")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB "
                          "(reference kernel for HBM byte counters)")
@@ -320,6 +322,50 @@ def copy_reference(reorder_gbs, mib=2048, reps=10):
             "frac_of_8TBs": round(gbs / 8000.0, 4), "reorder_over_copy": round(reorder_gbs / gbs, 4)}
 
 
+def mfma_ceiling(attn_tflops, iters=2_000_000):
+    """Matrix-core-only steady state of this card (libfva_probe.so): two waves
+    per SIMD issuing independent 32x32x16 bf16 MFMAs on register operands,
+    nothing else, for about half a second, on random normal operands and on
+    constant ones.  The switching power of the data sets the clock the matrix
+    cores can hold, so the rate on random operands is the practical ceiling
+    of any bf16 MFMA kernel on real data; the attention kernel's rate is also
+    given as a share of it.  The roofline's peak stays the published one."""
+    import ctypes
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "adaptive_block_sparse_reorder_amd", "libfva_probe.so"))
+    lib.fva_probe_operand_bytes.restype = ctypes.c_size_t
+    lib.fva_probe_output_bytes.restype = ctypes.c_size_t
+    lib.fva_probe_operand_bytes.argtypes = [ctypes.c_int32]
+    lib.fva_probe_output_bytes.argtypes = [ctypes.c_int32]
+    lib.fva_probe_mfma.restype = ctypes.c_int32
+    lib.fva_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_void_p]
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    nop = lib.fva_probe_operand_bytes(blocks) // 2
+    out = torch.empty(lib.fva_probe_output_bytes(blocks) // 4, dtype=torch.float32, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    res = {"what": "independent v_mfma_f32_32x32x16_bf16, 2 waves per SIMD, register operands, "
+                   f"{iters} rounds of 4 per wave"}
+    stream = torch.cuda.current_stream()
+    for name, ops in (("random", torch.randn(nop, device="cuda", dtype=torch.bfloat16, generator=gen)),
+                      ("constant", torch.ones(nop, device="cuda", dtype=torch.bfloat16))):
+        st = lib.fva_probe_mfma(ops.data_ptr(), out.data_ptr(), blocks, iters // 10, stream.cuda_stream)
+        assert st == 0, st
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        st = lib.fva_probe_mfma(ops.data_ptr(), out.data_ptr(), blocks, iters, stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        assert st == 0, st
+        ms = e0.elapsed_time(e1)
+        flop = blocks * 512 / 64 * iters * 4 * 32768.0
+        res[f"{name}_tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
+        res[f"{name}_ms"] = round(ms, 2)
+    res["attn_over_random"] = round(attn_tflops / res["random_tflops"], 4)
+    return res
+
+
 def gemm_reference(attn_tflops, n=8192, reps=50):
     """Practical bf16 MFMA rate of this card: the vendor GEMM (torch.matmul)
     on random normal operands.  Data-dependent power, not the issue rate, sets
@@ -433,6 +479,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     extras = {}
+    if args.no_extras and args.mfma_probe:
+        extras["mfma_ceiling"] = mfma_ceiling(attn_tflops)
     if not args.no_extras:
         log("dense comparator and schedule traces")
         # dense comparator, same core
@@ -450,6 +498,7 @@ def main():
         extras["dense_tflops"] = de_flop / (ms_dense * 1e-3) / 1e12
         extras["speedup_vs_dense"] = ms_dense / ms_attn
         extras["gemm_reference"] = gemm_reference(attn_tflops)
+        extras["mfma_ceiling"] = mfma_ceiling(attn_tflops)
         extras["torch_copy_reference"] = copy_reference(reorder_bytes / (ms_reorder * 1e-3) / 1e9)
         # mask recall: per-query log-sum-exp of the sparse and the dense kernel
         nq = w.B * w.Hh * w.N

@@ -141,3 +141,32 @@ def test_tile_table_sizes_and_limits(lib):
     assert lib.fva_tile_table_status(None, ctypes.byref(out), None) == F.FVA_ERR_INVALID_ARG
     assert lib.fva_tile_table_status(1028, ctypes.byref(out), None) == F.FVA_ERR_INVALID_ARG
     assert lib.fva_tile_table_status(1024, None, None) == F.FVA_ERR_INVALID_ARG
+
+
+def test_probe_library_exports_and_checks_arguments():
+    # the benchmark's matrix-core probe: a library of its own, every symbol its
+    # header declares exported, bad arguments refused before any launch
+    import re
+    path = os.path.join(os.path.dirname(F.LIB_PATH), "libfva_probe.so")
+    if not os.path.exists(path):
+        from adaptive_block_sparse_reorder_amd import build
+        build.build(verbose=False)
+    lib = ctypes.CDLL(path)
+    hdr = open(os.path.join(os.path.dirname(F.HEADER), "fva_probe.h")).read()
+    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    names = sorted(set(re.findall(r"\b(fva_probe_[a-z_]+)\s*\(", hdr)))
+    assert names == ["fva_probe_mfma", "fva_probe_operand_bytes", "fva_probe_output_bytes"]
+    for n in names:
+        assert hasattr(lib, n), n
+    lib.fva_probe_operand_bytes.restype = ctypes.c_size_t
+    lib.fva_probe_output_bytes.restype = ctypes.c_size_t
+    assert lib.fva_probe_operand_bytes(2) == 2 * 512 * 32
+    assert lib.fva_probe_output_bytes(2) == 2 * 512 * 4
+    assert lib.fva_probe_operand_bytes(0) == 0
+    f = lib.fva_probe_mfma
+    f.restype = ctypes.c_int32
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    assert f(None, 256, 1, 1, None) == -1
+    assert f(256, 256, 0, 1, None) == -1
+    assert f(256, 256, 1, 0, None) == -1
+    assert f(264, 256, 1, 1, None) == -1
