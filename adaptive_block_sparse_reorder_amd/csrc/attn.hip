@@ -109,7 +109,9 @@ struct AttnArgs {
   int64_t N, Npad;
   int64_t rows;
   int nB;
-  float sl2;  // scale * log2(e)
+  float sl2;   // scale * log2(e)
+  int direct;  // 1: queue entry i is row i (every item is resident at once, so
+               // the order of the queue buys nothing and its read is skipped)
 };
 
 // QT = 32-query tiles per wave (1: 4 waves of 32 queries per 128-row block,
@@ -197,15 +199,19 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_
     uint64_t t_start = 0;
     if (TRACE && tid == 0) t_start = __builtin_amdgcn_s_memrealtime();
     int64_t row;
-    if (DENSE || SCHED == FVA_SCHED_STATIC) row = item;
+    if (DENSE || SCHED == FVA_SCHED_STATIC || a.direct) row = item;
     else row = a.queue[item];
     row = __builtin_amdgcn_readfirstlane((int)row);
     const int64_t bh = row / a.nB;
     const int qb = (int)(row - bh * a.nB);
-    const int cnt = DENSE ? a.nB : __builtin_amdgcn_readfirstlane(a.row_count[row]);
+    int cnt = a.nB;
     if (!DENSE) {
+      // the count and the whole column row are read together (entries past
+      // the count are in bounds and never used), not one after the other
+      const int cnt_ld = a.row_count[row];
       const int16_t* cols = a.col_idx + row * a.nB;
-      for (int t = tid; t < cnt; t += NT) s_cols[t] = cols[t];
+      for (int t = tid; t < a.nB; t += NT) s_cols[t] = cols[t];
+      cnt = __builtin_amdgcn_readfirstlane(cnt_ld);
       __syncthreads();
     }
     const int64_t nlast = a.N - (int64_t)(a.nB - 1) * BLK;  // real keys of the last block
@@ -516,14 +522,23 @@ fva_status launch_t(const Problem& p, AttnArgs a, int flags, bool dense, hipStre
                        dim3(NT), 0, s, a);
     return hip_fail(hipGetLastError(), "dense attention launch");
   }
-  // persistent grid: as many workgroups as can be resident at once
+  // persistent grid: as many workgroups as can be resident at once (the
+  // occupancy query costs microseconds of host time, so it is asked once per
+  // device and kept)
   const int cus = device_cu_count();
-  int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &per_cu, reinterpret_cast<const void*>(&attn_kernel<D, BLK, kQT, FVA_SCHED_QUEUE, false, false>),
-      NT, 0);
-  if (e != hipSuccess) return hip_fail(e, "occupancy query");
-  if (per_cu < 1) per_cu = 1;
+  static int occ_cache[64] = {0};  // 0 = not asked yet; two racing callers store the same value
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "current device");
+  int per_cu = (dev >= 0 && dev < 64) ? __atomic_load_n(&occ_cache[dev], __ATOMIC_ACQUIRE) : 0;
+  if (per_cu == 0) {
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, reinterpret_cast<const void*>(&attn_kernel<D, BLK, kQT, FVA_SCHED_QUEUE, false, false>),
+        NT, 0);
+    if (e != hipSuccess) return hip_fail(e, "occupancy query");
+    if (per_cu < 1) per_cu = 1;
+    if (dev >= 0 && dev < 64) __atomic_store_n(&occ_cache[dev], per_cu, __ATOMIC_RELEASE);
+  }
   const int64_t slots = (int64_t)cus * per_cu;
   const int64_t persist = std::min<int64_t>(p.rows, slots);
 #define FVA_LAUNCH(SCH, TR, GRIDN)                                                         \
@@ -531,9 +546,11 @@ fva_status launch_t(const Problem& p, AttnArgs a, int flags, bool dense, hipStre
                      0, s, a)
   // When every item fits in one wave of resident workgroups, each persistent
   // workgroup of the queue and XCD schedules would run exactly one item: one
-  // plain launch over the heaviest-first queue does the same work without the
-  // counter reset or the XCD plan.
-  if ((sched == FVA_SCHED_QUEUE || sched == FVA_SCHED_XCD) && p.rows <= slots) {
+  // plain launch with workgroup i on row i does the same work without the
+  // counter reset, the XCD plan or the queue read (all items start at once,
+  // so their order does not matter).
+  if (sched != FVA_SCHED_STATIC && p.rows <= slots) {
+    a.direct = 1;
     if (trace) FVA_LAUNCH(FVA_SCHED_GRID, true, p.rows);
     else FVA_LAUNCH(FVA_SCHED_GRID, false, p.rows);
   } else if (sched == FVA_SCHED_QUEUE) {
@@ -607,6 +624,7 @@ fva_status launch_attn(const Problem& p, const void* qr, const void* kr, const v
   a.rows = p.rows;
   a.nB = p.nB;
   a.sl2 = scale * 1.4426950408889634f;
+  a.direct = 0;
   if (p.d == 128 && p.BLK == 128) return launch_t<128, 128>(p, a, flags, dense, s);
   if (p.d == 128 && p.BLK == 64) return launch_t<128, 64>(p, a, flags, dense, s);
   if (p.d == 64 && p.BLK == 128) return launch_t<64, 128>(p, a, flags, dense, s);

@@ -156,6 +156,30 @@ fva_status fva_reorder_ex(const void* src, void* dst, int32_t B, int32_t Hh, int
   return launch_reorder(p, src, dst, strides, direction, layout, (int32_t*)table, stream);
 }
 
+fva_status fva_reorder_pool(const void* src, void* dst, void* pooled, int32_t B, int32_t Hh,
+                            int32_t d, const fva_grid* grid, void* table,
+                            const int64_t strides[3], int32_t layout, hipStream_t stream) {
+  Problem p;
+  fva_status st = make_problem(grid, B, Hh, d, &p);
+  if (st != FVA_OK) return st;
+  if (!src || !dst || !pooled || !strides) return fail(FVA_ERR_INVALID_ARG, "null pointer");
+  if (layout != FVA_LAYOUT_ROWS && layout != FVA_LAYOUT_K64)
+    return fail(FVA_ERR_INVALID_ARG, "pooling reorder writes the rows or k64 layout, not %d",
+                layout);
+  for (int i = 0; i < 3; ++i)
+    if (strides[i] <= 0 || (strides[i] & 7))
+      return fail(FVA_ERR_INVALID_ARG, "stride %d = %lld must be a positive multiple of 8", i,
+                  (long long)strides[i]);
+  if (!aligned16(src) || !aligned16(dst) || !aligned16(pooled))
+    return fail(FVA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (strides[2] < d) return fail(FVA_ERR_INVALID_ARG, "head stride smaller than d");
+  if (table && tile_count(p) > kMaxTiles)
+    return fail(FVA_ERR_UNSUPPORTED, "%lld tiles exceed %d", (long long)tile_count(p), kMaxTiles);
+  if (table && !aligned16(table)) return fail(FVA_ERR_INVALID_ARG, "table must be 16-byte aligned");
+  return launch_reorder_pool(p, src, dst, (float*)pooled, strides, layout, (int32_t*)table,
+                             stream);
+}
+
 fva_status fva_reorder(const void* src, void* dst, int32_t B, int32_t Hh, int32_t d,
                        const fva_grid* grid, const int64_t strides[3], int32_t direction,
                        int32_t layout, hipStream_t stream) {
@@ -204,7 +228,10 @@ fva_status fva_route(const void* qr, const void* kr, int32_t B, int32_t Hh, int3
   fva_status st = make_problem(grid, B, Hh, d, &p);
   if (st != FVA_OK) return st;
   if (!params) return fail(FVA_ERR_INVALID_ARG, "params is null");
-  if (flags & ~FVA_ROUTE_SCORES_IN) return fail(FVA_ERR_INVALID_ARG, "flags 0x%x", flags);
+  if (flags & ~(FVA_ROUTE_SCORES_IN | FVA_ROUTE_POOLED_IN))
+    return fail(FVA_ERR_INVALID_ARG, "flags 0x%x", flags);
+  if ((flags & FVA_ROUTE_SCORES_IN) && (flags & FVA_ROUTE_POOLED_IN))
+    return fail(FVA_ERR_INVALID_ARG, "FVA_ROUTE_SCORES_IN and FVA_ROUTE_POOLED_IN exclude each other");
   const bool scores_in = (flags & FVA_ROUTE_SCORES_IN) != 0;
   if (!scores_in && (!qr || !kr)) return fail(FVA_ERR_INVALID_ARG, "qr/kr null");
   if (!scores_in && (!aligned16(qr) || !aligned16(kr)))

@@ -53,6 +53,8 @@ constexpr int kMaxXcdHeads = 4096;
 // Kernel launchers (each returns FVA_OK or FVA_ERR_HIP).
 fva_status launch_reorder(const Problem& p, const void* src, void* dst, const int64_t st[3],
                           int direction, int layout, int32_t* table, hipStream_t s);
+fva_status launch_reorder_pool(const Problem& p, const void* src, void* dst, float* pooled,
+                               const int64_t st[3], int layout, int32_t* table, hipStream_t s);
 fva_status launch_route(const Problem& p, const void* qr, const void* kr,
                         const fva_route_params& prm, float scale, const fva_mask& m,
                         char* ws, int flags, hipStream_t s);

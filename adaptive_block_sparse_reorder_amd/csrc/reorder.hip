@@ -89,6 +89,9 @@ constexpr int kThreads = 256;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
 __global__ __launch_bounds__(kThreads) void reorder_rows_fwd(
     const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, BlockOrder bo, int64_t N,
     int64_t Npad, int Hh, int d, int64_t sb, int64_t sn, int64_t sh) {
@@ -125,6 +128,75 @@ __global__ __launch_bounds__(kThreads) void reorder_rows_fwd(
       if (r >= Npad) continue;
       *(u32x4*)(dst + (((int64_t)b * Hh + h) * Npad + r) * d + c * 8) = v[j];
     }
+  }
+}
+
+// Forward rows that also write each block's mean over its real tokens (the
+// pooled block representative of section 3.1's routing, in float32).  One
+// workgroup per (block, group of kPoolHeads heads, batch): the block's source
+// token indices go to LDS once; thread (position class, head, 16-byte chunk)
+// copies positions p = class, class + PP, ... with the chunk fastest (a wave
+// reads kPoolHeads*2*d contiguous source bytes of a token and writes whole
+// 2*d-byte rows) and sums the real ones into eight float32 lanes; the PP
+// position classes are then added in class order.
+constexpr int kPoolHeads = 8;
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void reorder_rows_pool_fwd(
+    const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, float* __restrict__ pooled,
+    BlockOrder bo, int64_t N, int64_t Npad, int Hh, int BLK, int nB, int64_t sb, int64_t sn,
+    int64_t sh) {
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int UNITS = kPoolHeads * CPR;    // (head, chunk) units per position
+  constexpr int PP = kThreads / UNITS;       // position classes: 2 (d=128) or 4 (d=64)
+  constexpr int U = 4;                       // loads in flight per thread
+  __shared__ int64_t tok[128];
+  __shared__ float part[PP][kPoolHeads * D];
+  const int blk = blockIdx.x, h0 = blockIdx.y * kPoolHeads, b = blockIdx.z;
+  const int64_t r0 = (int64_t)blk * BLK;
+  const int nreal = (int)min((int64_t)BLK, N - r0);
+  for (int i = threadIdx.x; i < BLK; i += kThreads) tok[i] = i < nreal ? bo.src_token(r0 + i) : -1;
+  __syncthreads();
+  const int u = threadIdx.x % UNITS, cls = threadIdx.x / UNITS;
+  const int hl = u / CPR, c = u % CPR, h = h0 + hl;
+  const bool live = h < Hh;
+  const uint16_t* sp = src + b * sb + (int64_t)min(h, Hh - 1) * sh + c * 8;
+  uint16_t* dp = dst + (((int64_t)b * Hh + min(h, Hh - 1)) * Npad + r0) * D + c * 8;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int p0 = cls; p0 < BLK; p0 += PP * U) {
+    u32x4 v[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int pos = p0 + j * PP;
+      v[j] = u32x4{0u, 0u, 0u, 0u};
+      if (live && pos < BLK) {
+        const int64_t n = tok[pos];
+        if (n >= 0) v[j] = __builtin_nontemporal_load((const u32x4*)(sp + n * sn));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int pos = p0 + j * PP;
+      if (!live || pos >= BLK) continue;
+      *(u32x4*)(dp + (int64_t)pos * D) = v[j];
+      if (pos < nreal) {
+        acc[0] += bf16_lo(v[j].x); acc[1] += bf16_hi(v[j].x);
+        acc[2] += bf16_lo(v[j].y); acc[3] += bf16_hi(v[j].y);
+        acc[4] += bf16_lo(v[j].z); acc[5] += bf16_hi(v[j].z);
+        acc[6] += bf16_lo(v[j].w); acc[7] += bf16_hi(v[j].w);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[cls][u * 8 + e] = acc[e];
+  __syncthreads();
+  for (int o = threadIdx.x; o < kPoolHeads * D; o += kThreads) {
+    const int hh = h0 + o / D;
+    if (hh >= Hh) continue;
+    float sum = part[0][o];
+#pragma unroll
+    for (int q = 1; q < PP; ++q) sum += part[q][o];
+    pooled[(((int64_t)b * Hh + hh) * nB + blk) * D + (o % D)] = sum / (float)nreal;
   }
 }
 
@@ -174,58 +246,98 @@ __device__ __forceinline__ int v_slot(int k) {
 // 16 KB (d=128) tile in one contiguous, coalesced sweep.
 //   K64: unit (c, r) = channels 8c..8c+7 of token r, at unit index c*64 + r
 //   V64: unit (g, e) = channel e of the tokens in slots 8g..8g+7, at g*D + e
-template <int D, bool IS_V>
+// With POOL the workgroup owns a whole block (BLK/64 chunks, one after the
+// other) and also writes the block's mean over its real tokens: each thread
+// sums the rows it loaded (pad rows load as zero and are not added), then the
+// threads of one chunk column are added by shuffles and the four waves
+// through LDS, in a fixed order.
+template <int D, bool IS_V, bool POOL>
 __global__ __launch_bounds__(kThreads) void reorder_tile64_fwd(
-    const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, BlockOrder bo, int64_t N,
-    int64_t Npad, int Hh, int64_t sb, int64_t sn, int64_t sh) {
+    const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, float* __restrict__ pooled,
+    BlockOrder bo, int64_t N, int64_t Npad, int Hh, int BLK, int nB, int64_t sb, int64_t sn,
+    int64_t sh) {
+  static_assert(!(IS_V && POOL), "pooling is for the K layout");
   constexpr int kPitch = D + 8;
   __shared__ __attribute__((aligned(16))) uint16_t stage[64 * kPitch];
   __shared__ int64_t tok[64];
-  const int64_t chunk = blockIdx.x;  // 64-token chunk index within the head
+  __shared__ float part[POOL ? 4 : 1][POOL ? D : 1];
   const int bh = blockIdx.y;
   const int b = bh / Hh, h = bh % Hh;
-  const int64_t r0 = chunk * 64;
-  if (threadIdx.x < 64) {
-    const int64_t r = r0 + threadIdx.x;
-    tok[threadIdx.x] = r < N ? bo.src_token(r) : -1;
-  }
-  __syncthreads();
+  const int chunks = POOL ? BLK / 64 : 1;
   constexpr int cpr = D / 8;
   constexpr int kPer = 64 * cpr / kThreads;  // 16-byte loads per thread (4 at d=128)
   static_assert(kPer * kThreads == 64 * cpr, "chunk size");
-  u32x4 lv[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int L = threadIdx.x + j * kThreads;
-    const int c = L % cpr, k = L / cpr;
-    const int64_t n = tok[k];
-    lv[j] = u32x4{0u, 0u, 0u, 0u};
-    if (n >= 0) lv[j] = __builtin_nontemporal_load((const u32x4*)(src + b * sb + n * sn + h * sh + c * 8));
-  }
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int L = threadIdx.x + j * kThreads;
-    const int c = L % cpr, k = L / cpr;
-    *(u32x4*)(&stage[k * kPitch + c * 8]) = lv[j];
-  }
-  __syncthreads();
-  u32x4* out = (u32x4*)(dst + ((int64_t)bh * (Npad / 64) + chunk) * (int64_t)D * 64);
-  for (int u = threadIdx.x; u < 64 * cpr; u += kThreads) {
-    u32x4 v;
-    if (!IS_V) {
-      const int c = u / 64, r = u % 64;
-      v = *(const u32x4*)(&stage[r * kPitch + c * 8]);
-    } else {
-      const int g = u / D, e = u % D;
-      uint16_t vals[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) vals[q] = stage[v_slot(8 * g + q) * kPitch + e];
-      v.x = vals[0] | ((uint32_t)vals[1] << 16);
-      v.y = vals[2] | ((uint32_t)vals[3] << 16);
-      v.z = vals[4] | ((uint32_t)vals[5] << 16);
-      v.w = vals[6] | ((uint32_t)vals[7] << 16);
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int q = 0; q < chunks; ++q) {
+    const int64_t chunk = (int64_t)blockIdx.x * chunks + q;  // 64-token chunk within the head
+    const int64_t r0 = chunk * 64;
+    if (q > 0) __syncthreads();  // the previous chunk's LDS reads are done
+    if (threadIdx.x < 64) {
+      const int64_t r = r0 + threadIdx.x;
+      tok[threadIdx.x] = r < N ? bo.src_token(r) : -1;
     }
-    out[u] = v;
+    __syncthreads();
+    u32x4 lv[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int L = threadIdx.x + j * kThreads;
+      const int c = L % cpr, k = L / cpr;
+      const int64_t n = tok[k];
+      lv[j] = u32x4{0u, 0u, 0u, 0u};
+      if (n >= 0) lv[j] = __builtin_nontemporal_load((const u32x4*)(src + b * sb + n * sn + h * sh + c * 8));
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int L = threadIdx.x + j * kThreads;
+      const int c = L % cpr, k = L / cpr;
+      *(u32x4*)(&stage[k * kPitch + c * 8]) = lv[j];
+      if (POOL && r0 + k < N) {
+        acc[0] += bf16_lo(lv[j].x); acc[1] += bf16_hi(lv[j].x);
+        acc[2] += bf16_lo(lv[j].y); acc[3] += bf16_hi(lv[j].y);
+        acc[4] += bf16_lo(lv[j].z); acc[5] += bf16_hi(lv[j].z);
+        acc[6] += bf16_lo(lv[j].w); acc[7] += bf16_hi(lv[j].w);
+      }
+    }
+    __syncthreads();
+    u32x4* out = (u32x4*)(dst + ((int64_t)bh * (Npad / 64) + chunk) * (int64_t)D * 64);
+    for (int u = threadIdx.x; u < 64 * cpr; u += kThreads) {
+      u32x4 v;
+      if (!IS_V) {
+        const int c = u / 64, r = u % 64;
+        v = *(const u32x4*)(&stage[r * kPitch + c * 8]);
+      } else {
+        const int g = u / D, e = u % D;
+        uint16_t vals[8];
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq) vals[qq] = stage[v_slot(8 * g + qq) * kPitch + e];
+        v.x = vals[0] | ((uint32_t)vals[1] << 16);
+        v.y = vals[2] | ((uint32_t)vals[3] << 16);
+        v.z = vals[4] | ((uint32_t)vals[5] << 16);
+        v.w = vals[6] | ((uint32_t)vals[7] << 16);
+      }
+      out[u] = v;
+    }
+  }
+  if (POOL) {
+    // lanes l, l ^ cpr, l ^ 2cpr, ... of a wave hold the same channel chunk
+    const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+#pragma unroll
+    for (int off = cpr; off < 64; off <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
+    }
+    if (lane < cpr) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[wave][lane * 8 + e] = acc[e];
+    }
+    __syncthreads();
+    if (threadIdx.x < D) {
+      const int64_t rb = (int64_t)blockIdx.x * BLK;
+      const int nreal = (int)min((int64_t)BLK, N - rb);
+      const float sum = (part[0][threadIdx.x] + part[1][threadIdx.x]) +
+                        (part[2][threadIdx.x] + part[3][threadIdx.x]);
+      pooled[((int64_t)bh * nB + blockIdx.x) * D + threadIdx.x] = sum / (float)nreal;
+    }
   }
 }
 
@@ -363,9 +475,9 @@ fva_status launch_reorder(const Problem& p, const void* src, void* dst, const in
   } else {
     dim3 grid((unsigned)(p.Npad / 64), (unsigned)(p.B * p.Hh));
     const bool v = layout == FVA_LAYOUT_V64;
-#define FVA_TILE_LAUNCH(DD, VV)                                                               \
-  hipLaunchKernelGGL((reorder_tile64_fwd<DD, VV>), grid, dim3(kThreads), 0, s, in, out, bo, p.N, \
-                     p.Npad, p.Hh, st[0], st[1], st[2])
+#define FVA_TILE_LAUNCH(DD, VV)                                                                 \
+  hipLaunchKernelGGL((reorder_tile64_fwd<DD, VV, false>), grid, dim3(kThreads), 0, s, in, out,  \
+                     nullptr, bo, p.N, p.Npad, p.Hh, p.BLK, p.nB, st[0], st[1], st[2])
     if (p.d == 128) {
       if (v) FVA_TILE_LAUNCH(128, true);
       else FVA_TILE_LAUNCH(128, false);
@@ -376,6 +488,31 @@ fva_status launch_reorder(const Problem& p, const void* src, void* dst, const in
 #undef FVA_TILE_LAUNCH
   }
   return hip_fail(hipGetLastError(), "reorder launch");
+}
+
+fva_status launch_reorder_pool(const Problem& p, const void* src, void* dst, float* pooled,
+                               const int64_t st[3], int layout, int32_t* table, hipStream_t s) {
+  BlockOrder bo{p.T, p.H, p.W, p.bt, p.bh, p.bw, table, (int32_t)tile_count(p)};
+  const uint16_t* in = (const uint16_t*)src;
+  uint16_t* out = (uint16_t*)dst;
+  if (layout == FVA_LAYOUT_ROWS) {
+    dim3 grid((unsigned)p.nB, (unsigned)((p.Hh + kPoolHeads - 1) / kPoolHeads), (unsigned)p.B);
+    if (p.d == 128)
+      hipLaunchKernelGGL(reorder_rows_pool_fwd<128>, grid, dim3(kThreads), 0, s, in, out, pooled,
+                         bo, p.N, p.Npad, p.Hh, p.BLK, p.nB, st[0], st[1], st[2]);
+    else
+      hipLaunchKernelGGL(reorder_rows_pool_fwd<64>, grid, dim3(kThreads), 0, s, in, out, pooled,
+                         bo, p.N, p.Npad, p.Hh, p.BLK, p.nB, st[0], st[1], st[2]);
+  } else {
+    dim3 grid((unsigned)p.nB, (unsigned)(p.B * p.Hh));
+    if (p.d == 128)
+      hipLaunchKernelGGL((reorder_tile64_fwd<128, false, true>), grid, dim3(kThreads), 0, s, in,
+                         out, pooled, bo, p.N, p.Npad, p.Hh, p.BLK, p.nB, st[0], st[1], st[2]);
+    else
+      hipLaunchKernelGGL((reorder_tile64_fwd<64, false, true>), grid, dim3(kThreads), 0, s, in,
+                         out, pooled, bo, p.N, p.Npad, p.Hh, p.BLK, p.nB, st[0], st[1], st[2]);
+  }
+  return hip_fail(hipGetLastError(), "reorder with pooling launch");
 }
 
 }  // namespace fva

@@ -520,7 +520,12 @@ __global__ __launch_bounds__(kQThreads) void queue_chunk_kernel(
                           ? ((uint32_t)(nB - row_count[item]) << 10) | (uint32_t)threadIdx.x
                           : 0xffffffffu;
   __syncthreads();
-  bitonic_sort<uint32_t, kQThreads>(keys, kQThreads);
+  // only the chunk's real rows need sorting: the first power of two that
+  // holds them (the rest are all-ones keys, already in place at the end)
+  const int64_t nreal = min((int64_t)kQThreads, rows - base);
+  int P = 2;
+  while (P < nreal) P <<= 1;
+  bitonic_sort<uint32_t, kQThreads>(keys, P);
   const uint32_t k = keys[threadIdx.x];
   const bool valid = k != 0xffffffffu;
   const uint32_t grp = k >> 10;
@@ -639,19 +644,25 @@ fva_status launch_route(const Problem& p, const void* qr, const void* kr,
                         char* ws, int flags, hipStream_t s) {
   const RouteWs L = route_ws_layout(p);
   uint32_t* wflags = (uint32_t*)(ws + L.flags_off);
-  float* qbar = (float*)(ws + L.qbar_off);
-  float* kbar = (float*)(ws + L.kbar_off);
+  const bool pooled_in = (flags & FVA_ROUTE_POOLED_IN) != 0;
+  // block means: the workspace's, or the caller's (written by fva_reorder_pool)
+  const float* qbar = pooled_in ? (const float*)qr : (const float*)(ws + L.qbar_off);
+  const float* kbar = pooled_in ? (const float*)kr : (const float*)(ws + L.kbar_off);
   const int nheads = p.B * p.Hh;
   hipLaunchKernelGGL(zero_route_state, dim3((nheads + 255) / 256), dim3(256), 0, s,
                      m.head_count, nheads, wflags);
   if (!(flags & FVA_ROUTE_SCORES_IN)) {
     dim3 pg(p.nB, nheads, 2);
-    if (p.d == 128)
+    float* qw = (float*)(ws + L.qbar_off);
+    float* kw = (float*)(ws + L.kbar_off);
+    if (pooled_in) {
+      // nothing to pool
+    } else if (p.d == 128)
       hipLaunchKernelGGL(pool_kernel<128>, pg, dim3(256), 0, s, (const uint16_t*)qr,
-                         (const uint16_t*)kr, qbar, kbar, p.N, p.Npad, p.BLK, p.nB);
+                         (const uint16_t*)kr, qw, kw, p.N, p.Npad, p.BLK, p.nB);
     else
       hipLaunchKernelGGL(pool_kernel<64>, pg, dim3(256), 0, s, (const uint16_t*)qr,
-                         (const uint16_t*)kr, qbar, kbar, p.N, p.Npad, p.BLK, p.nB);
+                         (const uint16_t*)kr, qw, kw, p.N, p.Npad, p.BLK, p.nB);
     dim3 sg((p.nB + 63) / 64, (p.nB + 63) / 64, nheads);
     if (p.d == 128)
       hipLaunchKernelGGL(score_kernel<128>, sg, dim3(256), 0, s, qbar, kbar, m.scores, p.nB,

@@ -26,6 +26,7 @@ FVA_ERR_WORKSPACE = -3
 FVA_ERR_HIP = -4
 
 FVA_ROUTE_SCORES_IN = 0x1
+FVA_ROUTE_POOLED_IN = 0x2
 FVA_SCHED_QUEUE = 0x0
 FVA_SCHED_STATIC = 0x1
 FVA_SCHED_GRID = 0x2
@@ -107,6 +108,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                             ctypes.POINTER(fva_mask), F, I32, P, P, P]
     lib.fva_reorder_ex.argtypes = [P, P, I32, I32, I32, ctypes.POINTER(fva_grid), P,
                                    ctypes.POINTER(ctypes.c_int64), I32, I32, P]
+    lib.fva_reorder_pool.argtypes = [P, P, P, I32, I32, I32, ctypes.POINTER(fva_grid), P,
+                                     ctypes.POINTER(I64), I32, P]
     lib.fva_tile_order_bytes.argtypes = [ctypes.POINTER(fva_grid), ctypes.POINTER(ctypes.c_size_t)]
     lib.fva_tile_order.argtypes = [ctypes.POINTER(fva_grid), I32, P, SZ, P]
     lib.fva_tile_table_status.argtypes = [P, ctypes.POINTER(ctypes.c_int32), P]
@@ -119,7 +122,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                               ctypes.POINTER(fva_mask), P, SZ, P]
     for fn in ("fva_sizes", "fva_reorder", "fva_route", "fva_route_flags", "fva_sparse_attn",
                "fva_dense_attn", "fva_rlb_plan", "fva_sasa_budget", "fva_topup",
-               "fva_reorder_ex", "fva_tile_order_bytes", "fva_tile_order",
+               "fva_reorder_ex", "fva_reorder_pool", "fva_tile_order_bytes", "fva_tile_order",
                "fva_tile_table_status", "fva_sparse_attn_noalloc"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.fva_status_string.argtypes = [ctypes.c_int]
@@ -184,6 +187,16 @@ def fva_reorder_ex(src, dst, B: int, Hh: int, d: int, grid: fva_grid, table,
     st = (ctypes.c_int64 * 3)(*[int(s) for s in strides])
     _check(lib.fva_reorder_ex(_ptr(src), _ptr(dst), B, Hh, d, ctypes.byref(grid), _ptr(table), st,
                               direction, layout, _stream(stream)), "fva_reorder_ex")
+
+
+def fva_reorder_pool(src, dst, pooled, B: int, Hh: int, d: int, grid: fva_grid, table,
+                     strides: Sequence[int], layout: int = FVA_LAYOUT_ROWS, stream=None):
+    """Forward reorder into `layout` (rows or k64) that also writes the float32
+    block means [B*Hh, nB, d] into `pooled`."""
+    lib = load_library()
+    st = (ctypes.c_int64 * 3)(*[int(s) for s in strides])
+    _check(lib.fva_reorder_pool(_ptr(src), _ptr(dst), _ptr(pooled), B, Hh, d, ctypes.byref(grid),
+                                _ptr(table), st, layout, _stream(stream)), "fva_reorder_pool")
 
 
 def fva_tile_order_bytes(grid: fva_grid) -> int:
@@ -332,6 +345,8 @@ class Buffers:
     route_ws: object
     attn_ws: object
     trace: object
+    qbar: object = None
+    kbar: object = None
 
     def mask(self) -> fva_mask:
         return fva_mask(self.scores.data_ptr(), self.bitmask.data_ptr(),
@@ -363,7 +378,8 @@ def alloc_buffers(grid: Sequence[int], block: Sequence[int], B: int, Hh: int, d:
         row_count=dev((rows,), torch.int32), col_idx=dev((rows, nB), torch.int16),
         head_count=dev((B * Hh,), torch.int32), queue=dev((rows,), torch.int32),
         route_ws=ws(sz.route_ws_bytes), attn_ws=ws(sz.attn_ws_bytes),
-        trace=ws(sz.trace_bytes) if trace else None)
+        trace=ws(sz.trace_bytes) if trace else None,
+        qbar=dev((rows, d), torch.float32), kbar=dev((rows, d), torch.float32))
 
 
 def token_strides(x) -> Sequence[int]:
@@ -375,22 +391,36 @@ def token_strides(x) -> Sequence[int]:
 def forward(buf: Buffers, q, k, v, top_p: float, topk_floor: int, aug_budget: int = 0,
             scale: float = 0.0, route_flags: int = 0, attn_flags: int = FVA_SCHED_XCD,
             stream=None, table=None, lse=None):
-    """One pass of the hot path: reorder Q (rows), K (k64), V (v64) -> route -> block-sparse
-    attention -> inverse reorder.  Inputs [B, N, Hh, d] bf16 on the device;
+    """One pass of the hot path: reorder Q (rows) and K (k64) with their block
+    means, V (v64) -> route from the means -> block-sparse attention -> inverse
+    reorder (with FVA_ROUTE_SCORES_IN in route_flags: plain reorders, routing
+    from buf.scores as given).  Inputs [B, N, Hh, d] bf16 on the device;
     the result lands in buf.out.  `table`: a device tile table from
     fva_tile_order (None = raster tile order).  `lse`: optional float32 device
     tensor of B*Hh*N entries for each query's log-sum-exp (reordered positions)."""
     g, B, Hh, d = buf.grid, buf.B, buf.Hh, buf.d
-    fva_reorder_ex(q, buf.qr, B, Hh, d, g, table, token_strides(q), FVA_FORWARD,
-                   FVA_LAYOUT_ROWS, stream)
-    fva_reorder_ex(k, buf.kr, B, Hh, d, g, table, token_strides(k), FVA_FORWARD,
-                   FVA_LAYOUT_K64, stream)
+    pool = not (route_flags & FVA_ROUTE_SCORES_IN)
+    if pool:
+        # Q and K are pooled while they are reordered; the router reads the means
+        fva_reorder_pool(q, buf.qr, buf.qbar, B, Hh, d, g, table, token_strides(q),
+                         FVA_LAYOUT_ROWS, stream)
+        fva_reorder_pool(k, buf.kr, buf.kbar, B, Hh, d, g, table, token_strides(k),
+                         FVA_LAYOUT_K64, stream)
+    else:
+        fva_reorder_ex(q, buf.qr, B, Hh, d, g, table, token_strides(q), FVA_FORWARD,
+                       FVA_LAYOUT_ROWS, stream)
+        fva_reorder_ex(k, buf.kr, B, Hh, d, g, table, token_strides(k), FVA_FORWARD,
+                       FVA_LAYOUT_K64, stream)
     fva_reorder_ex(v, buf.vt, B, Hh, d, g, table, token_strides(v), FVA_FORWARD,
                    FVA_LAYOUT_V64, stream)
     prm = fva_route_params(top_p, topk_floor, aug_budget, scale, 0)
     m = buf.mask()
-    fva_route(buf.qr, buf.kr, B, Hh, d, g, prm, m, buf.route_ws, buf.sizes.route_ws_bytes,
-              route_flags, stream)
+    if pool:
+        fva_route(buf.qbar, buf.kbar, B, Hh, d, g, prm, m, buf.route_ws,
+                  buf.sizes.route_ws_bytes, route_flags | FVA_ROUTE_POOLED_IN, stream)
+    else:
+        fva_route(buf.qr, buf.kr, B, Hh, d, g, prm, m, buf.route_ws, buf.sizes.route_ws_bytes,
+                  route_flags, stream)
     fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, B, Hh, d, g, m, scale, attn_flags,
                     buf.attn_ws, buf.sizes.attn_ws_bytes,
                     buf.trace if (attn_flags & FVA_TRACE) else None, stream, lse=lse)

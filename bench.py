@@ -161,6 +161,18 @@ def cpu_baseline(w, q, k, v, seconds):
     }
 
 
+def reorder_pooled(F, w, buf, qd, kd, vd, table=None):
+    """Forward block organization of Q (rows) and K (k64) with their block
+    means written on the way, and of V (v64)."""
+    g = buf.grid
+    F.fva_reorder_pool(qd, buf.qr, buf.qbar, w.B, w.Hh, w.d, g, table, F.token_strides(qd),
+                       F.FVA_LAYOUT_ROWS)
+    F.fva_reorder_pool(kd, buf.kr, buf.kbar, w.B, w.Hh, w.d, g, table, F.token_strides(kd),
+                       F.FVA_LAYOUT_K64)
+    F.fva_reorder_ex(vd, buf.vt, w.B, w.Hh, w.d, g, table, F.token_strides(vd), F.FVA_FORWARD,
+                     F.FVA_LAYOUT_V64)
+
+
 def config_block(name, sched_flag, cus, slots, reps=3):
     """The whole path on another workload, timed stage by stage with HIP events
     on the launch stream (median of `reps` passes after two warm passes), with
@@ -188,9 +200,7 @@ def config_block(name, sched_flag, cus, slots, reps=3):
         return e
 
     def reorders():
-        for x, dst, lay in ((qd, buf.qr, F.FVA_LAYOUT_ROWS), (kd, buf.kr, F.FVA_LAYOUT_K64),
-                            (vd, buf.vt, F.FVA_LAYOUT_V64)):
-            F.fva_reorder(x, dst, w.B, w.Hh, w.d, g, F.token_strides(x), F.FVA_FORWARD, lay)
+        reorder_pooled(F, w, buf, qd, kd, vd)
 
     def attn(flags, trace=None):
         F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, g, m, 0.0, flags,
@@ -205,8 +215,8 @@ def config_block(name, sched_flag, cus, slots, reps=3):
         e = [event()]
         reorders()
         e.append(event())
-        F.fva_route(buf.qr, buf.kr, w.B, w.Hh, w.d, g, prm, m, buf.route_ws,
-                    buf.sizes.route_ws_bytes, 0)
+        F.fva_route(buf.qbar, buf.kbar, w.B, w.Hh, w.d, g, prm, m, buf.route_ws,
+                    buf.sizes.route_ws_bytes, F.FVA_ROUTE_POOLED_IN)
         e.append(event())
         attn(sched_flag)
         e.append(event())
@@ -428,14 +438,10 @@ def main():
 
     def step(timed):
         if timed: mark("s0")
-        F.fva_reorder(qd, buf.qr, w.B, w.Hh, w.d, g, F.token_strides(qd))
-        F.fva_reorder(kd, buf.kr, w.B, w.Hh, w.d, g, F.token_strides(kd), F.FVA_FORWARD,
-                      F.FVA_LAYOUT_K64)
-        F.fva_reorder(vd, buf.vt, w.B, w.Hh, w.d, g, F.token_strides(vd), F.FVA_FORWARD,
-                      F.FVA_LAYOUT_V64)
+        reorder_pooled(F, w, buf, qd, kd, vd)
         if timed: mark("s1")
-        F.fva_route(buf.qr, buf.kr, w.B, w.Hh, w.d, g, prm, m, buf.route_ws,
-                    buf.sizes.route_ws_bytes, 0)
+        F.fva_route(buf.qbar, buf.kbar, w.B, w.Hh, w.d, g, prm, m, buf.route_ws,
+                    buf.sizes.route_ws_bytes, F.FVA_ROUTE_POOLED_IN)
         if timed: mark("s2")
         F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, g, m, 0.0,
                           args.sched, buf.attn_ws, buf.sizes.attn_ws_bytes, None)
@@ -465,8 +471,9 @@ def main():
     ex_flop = F.executed_flops(nnz, w.d, w.BLK)
     de_flop = F.dense_equiv_flops(w.N, w.d, w.Hh, w.B)
     attn_tflops = ex_flop / (ms_attn * 1e-3) / 1e12
-    # reorder: read N*Hh*d and write Npad*Hh*d bf16 for each of Q, K, V
-    reorder_bytes = 3 * 2 * w.B * w.Hh * w.d * (w.N + w.Npad)
+    # reorder: read N*Hh*d and write Npad*Hh*d bf16 for each of Q, K, V, and
+    # write the float32 block means of Q and K
+    reorder_bytes = 3 * 2 * w.B * w.Hh * w.d * (w.N + w.Npad) + 2 * 4 * int(buf.sizes.rows) * w.d
     unre_bytes = 2 * w.B * w.Hh * w.d * (w.N + w.N)
 
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step, attention {ms_attn:.3f} ms")
@@ -526,6 +533,27 @@ def main():
         extras["lambda_cu"] = lam
 
     if not args.no_extras:
+        # reorder + route with the router pooling Q and K itself (a second
+        # read of both) against the pooling reorder the step uses
+        pev = []
+        for _ in range(3):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            for x, dst, lay in ((qd, buf.qr, F.FVA_LAYOUT_ROWS), (kd, buf.kr, F.FVA_LAYOUT_K64),
+                                (vd, buf.vt, F.FVA_LAYOUT_V64)):
+                F.fva_reorder(x, dst, w.B, w.Hh, w.d, g, F.token_strides(x), F.FVA_FORWARD, lay)
+            e[1].record(stream)
+            F.fva_route(buf.qr, buf.kr, w.B, w.Hh, w.d, g, prm, m, buf.route_ws,
+                        buf.sizes.route_ws_bytes, 0)
+            e[2].record(stream)
+            pev.append(e)
+        torch.cuda.synchronize()
+        extras["pool_in_router"] = {
+            "reorder_qkv_ms": round(float(np.median([e[0].elapsed_time(e[1]) for e in pev])), 4),
+            "route_ms": round(float(np.median([e[1].elapsed_time(e[2]) for e in pev])), 4),
+        }
+
+    if not args.no_extras:
         # the same step with the tile order along a 3-D Hilbert curve
         table = F.tile_table(g, F.FVA_ORDER_HILBERT)
         ev.clear()
@@ -534,13 +562,10 @@ def main():
                       table=table)
         hev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
         hev[0].record(stream)
-        for x, dst, lay in ((qd, buf.qr, F.FVA_LAYOUT_ROWS), (kd, buf.kr, F.FVA_LAYOUT_K64),
-                            (vd, buf.vt, F.FVA_LAYOUT_V64)):
-            F.fva_reorder_ex(x, dst, w.B, w.Hh, w.d, g, table, F.token_strides(x),
-                             F.FVA_FORWARD, lay)
+        reorder_pooled(F, w, buf, qd, kd, vd, table)
         hev[1].record(stream)
-        F.fva_route(buf.qr, buf.kr, w.B, w.Hh, w.d, g, prm, m, buf.route_ws,
-                    buf.sizes.route_ws_bytes, 0)
+        F.fva_route(buf.qbar, buf.kbar, w.B, w.Hh, w.d, g, prm, m, buf.route_ws,
+                    buf.sizes.route_ws_bytes, F.FVA_ROUTE_POOLED_IN)
         hev[2].record(stream)
         F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, g, m, 0.0,
                           args.sched, buf.attn_ws, buf.sizes.attn_ws_bytes, None)
@@ -706,6 +731,8 @@ def main():
             "dense_equiv_tflops": round(de_flop / (ms_attn * 1e-3) / 1e12, 2),
             "density": {"mean": float(heads.mean()), "min": float(heads.min()),
                         "max": float(heads.max())},
+            "stages": ("reorder_qkv: Q and K reordered with their block means, V reordered; "
+                       "route: block scores, Top-p/Top-k cut, mask, top-up, queue"),
             "reorder_qkv_ms": round(ms_reorder, 4),
             "reorder_qkv_GBs": round(reorder_bytes / (ms_reorder * 1e-3) / 1e9, 1),
             "route_ms": round(ms_route, 4),

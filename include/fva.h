@@ -107,6 +107,9 @@ typedef struct {
 /* fva_route flags */
 #define FVA_ROUTE_SCORES_IN 0x1  /* skip pooling and scoring: route from
                                     mask->scores as given                    */
+#define FVA_ROUTE_POOLED_IN 0x2  /* skip pooling: qr and kr point to the
+                                    float32 block means [B*Hh, nB, d] of Q and
+                                    K that fva_reorder_pool wrote            */
 
 /* fva_sparse_attn flags: schedule of (head, query-block) work items */
 #define FVA_SCHED_QUEUE  0x0  /* persistent workgroups pop the heaviest-first
@@ -184,15 +187,32 @@ fva_status fva_reorder_ex(const void* src, void* dst, int32_t B, int32_t Hh, int
                           const fva_grid* grid, void* table, const int64_t strides[3],
                           int32_t direction, int32_t layout, hipStream_t stream);
 
+/* Forward block organization (as fva_reorder_ex, FVA_FORWARD) that also
+ * writes the block means the router pools (sections 2 and 3.1): pooled
+ * (DEVICE, float32 [B*Hh, nB, d], 16-byte aligned, caller-owned) gets, for
+ * every head (b, h) and block i, the mean over the block's real tokens of
+ * their d channels (pad positions are not counted), summed in float32.
+ * layout: FVA_LAYOUT_ROWS (for Q) or FVA_LAYOUT_K64 (for K); dst is written
+ * exactly as fva_reorder_ex writes it.  table: NULL (raster tile order) or a
+ * tile table of this grid, checked as for fva_reorder_ex (positions that
+ * cannot be placed get zeros in dst and count as zero rows in their block's
+ * mean).  Pass the two means to fva_route with FVA_ROUTE_POOLED_IN in
+ * place of qr and kr; this saves the router's second read of Q and K.      */
+fva_status fva_reorder_pool(const void* src, void* dst, void* pooled, int32_t B, int32_t Hh,
+                            int32_t d, const fva_grid* grid, void* table,
+                            const int64_t strides[3], int32_t layout, hipStream_t stream);
+
 /* Copies a tile table's status word (0 = every lookup so far was consistent,
  * 1 = a reorder found the table does not belong to its grid) to *status_out
  * (host), synchronously on `stream`.                                        */
 fva_status fva_tile_table_status(const void* table, int32_t* status_out, hipStream_t stream);
 
 /* Sparse-routing frontend (sections 2 and 3.1; top-up section 3.3).
- * qr: `rows` bf16, kr: `k64` bf16.  For every row (b, h, i):
+ * qr: `rows` bf16, kr: `k64` bf16 (with FVA_ROUTE_POOLED_IN: the float32
+ * block means of Q and K from fva_reorder_pool).  For every row (b, h, i):
  *   1. unless FVA_ROUTE_SCORES_IN: qbar, kbar = mean of each block's real
- *      tokens; scores[r, j] = (qbar_i . kbar_j) * scale in float32;
+ *      tokens (read from qr and kr with FVA_ROUTE_POOLED_IN);
+ *      scores[r, j] = (qbar_i . kbar_j) * scale in float32;
  *   2. importance order = key blocks by score descending, ties by index
  *      ascending (-0 == +0);
  *   3. float64 softmax of the row accumulated along that order; the Top-p set

@@ -257,6 +257,74 @@ def test_pool_and_scores_close_to_oracle(entry):
     assert np.all(margins[differ] < 1e-4), margins[differ]
 
 
+@pytest.mark.parametrize("order", ["raster", "hilbert"])
+@pytest.mark.parametrize("entry", SMALL, ids=[e[0] for e in SMALL])
+def test_reorder_pool_layouts_bit_exact_and_means_close(entry, order):
+    # fva_reorder_pool writes the rows / k64 layouts bit for bit as the plain
+    # reorder does, plus float32 block means over real tokens; routing from
+    # those means (FVA_ROUTE_POOLED_IN) matches the oracle like routing from
+    # the reordered tensors does
+    w = _wl(entry)
+    q, k, v, qd, kd, vd, buf = setup(w)
+    g = buf.grid
+    table = F.tile_table(g, F.FVA_ORDER_HILBERT) if order == "hilbert" else None
+    for x, dst, pooled, lay in ((qd, buf.qr, buf.qbar, F.FVA_LAYOUT_ROWS),
+                                (kd, buf.kr, buf.kbar, F.FVA_LAYOUT_K64)):
+        dst.fill_(float("nan"))
+        pooled.fill_(float("nan"))
+        F.fva_reorder_pool(x, dst, pooled, w.B, w.Hh, w.d, g, table, F.token_strides(x), lay)
+    torch.cuda.synchronize()
+    qref = O.reorder(q.view(torch.int16).numpy(), w.grid, w.block, order)
+    kref = O.reorder(k.view(torch.int16).numpy(), w.grid, w.block, order)
+    assert np.array_equal(bits(buf.qr), qref)
+    assert np.array_equal(bits(buf.kr), k64_expected(kref))
+    qr = O.reorder(q.float().numpy(), w.grid, w.block, order)
+    kr = O.reorder(k.float().numpy(), w.grid, w.block, order)
+    for got, xr in ((buf.qbar, qr), (buf.kbar, kr)):
+        want = O.pool(xr, w.N, w.BLK).reshape(-1, w.d)
+        g_np = got.cpu().numpy()
+        # float32 sums of at most 128 bf16 values against float64
+        tol = 1e-5 * max(1.0, float(np.abs(xr).max()))
+        assert np.all(np.isfinite(g_np))
+        assert np.abs(g_np - want).max() <= tol
+    if table is not None:
+        F.fva_reorder_ex(vd, buf.vt, w.B, w.Hh, w.d, g, table, F.token_strides(vd),
+                         F.FVA_FORWARD, F.FVA_LAYOUT_V64)
+    prm = F.fva_route_params(w.top_p, w.topk_floor, w.aug_budget, 0.0, 0)
+    F.fva_route(buf.qbar, buf.kbar, w.B, w.Hh, w.d, g, prm, buf.mask(), buf.route_ws,
+                buf.sizes.route_ws_bytes, F.FVA_ROUTE_POOLED_IN)
+    torch.cuda.synchronize()
+    r = O.route_path(qr, kr, w.N, w.BLK, w.scale, w.top_p, w.topk_floor, w.aug_budget)
+    S = buf.scores.cpu().numpy().reshape(r["scores"].shape)
+    tol = 1e-5 * max(1.0, float(np.abs(r["scores"]).max()))
+    assert np.abs(S - r["scores"]).max() <= tol
+    differ = (unpack_bitmask(buf.bitmask, w.nB) != r["mask"].reshape(-1, w.nB)).any(axis=1)
+    assert differ.mean() <= 0.02
+    assert np.all(r["margin"].reshape(-1)[differ] < 1e-4)
+    assert F.fva_route_flags(buf.route_ws) == 0
+    if table is not None:
+        assert F.fva_tile_table_status(table) == 0
+
+
+def test_reorder_pool_with_a_table_of_another_grid_stays_in_bounds():
+    # the pooling reorder checks the tile table like the plain one: nothing is
+    # read outside it, unplaceable positions are zero rows, the status word is
+    # raised, and every mean is still written (finite)
+    w = SMALL[3][1]
+    q, k, v, qd, kd, vd, buf = setup(w)
+    g = buf.grid
+    other = F.tile_table(F.make_grid((3, 16, 17), w.block), F.FVA_ORDER_HILBERT)
+    for x, dst, pooled, lay in ((qd, buf.qr, buf.qbar, F.FVA_LAYOUT_ROWS),
+                                (kd, buf.kr, buf.kbar, F.FVA_LAYOUT_K64)):
+        dst.fill_(float("nan"))
+        pooled.fill_(float("nan"))
+        F.fva_reorder_pool(x, dst, pooled, w.B, w.Hh, w.d, g, other, F.token_strides(x), lay)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(dst).item() == 0, lay
+        assert torch.count_nonzero(pooled).item() == 0, lay
+    assert F.fva_tile_table_status(other) == 1
+
+
 # ----------------------------------------------------------------- attention
 
 def _oracle_attention(w, q, k, v, mask):
