@@ -48,6 +48,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int KT = 64;           // keys per sub-tile
+constexpr int kColChunk = 2048;  // column-list entries staged in LDS at a time
 constexpr int NXCD = 8;          // XCDs; workgroup b is dispatched to XCD b % 8
 constexpr float kLazy = 8.0f;    // log2-domain slack before the reference max moves
 
@@ -119,7 +120,10 @@ struct AttnArgs {
 template <int QT>
 constexpr int attn_threads(int blk) { return blk / (32 * QT) * 64; }
 
-template <int D, int BLK, int QT, int SCHED, bool DENSE, bool TRACE>
+// CHUNKED: rows may select more than kColChunk blocks, so the column list
+// is walked in LDS chunks (launched only when nB > kColChunk; otherwise the
+// walk is one straight pass over a list read whole).
+template <int D, int BLK, int QT, int SCHED, bool DENSE, bool TRACE, bool CHUNKED>
 __global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_per_eu(
     QT == 1 ? 2 : 1, QT == 1 ? 2 : 1))) void attn_kernel(AttnArgs a) {
   constexpr int NT = attn_threads<QT>(BLK);  // threads: BLK/(32*QT) waves
@@ -133,7 +137,7 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_
   static_assert(LOADS * 16 * NT == TILE, "tile size");
   // LDS: K tiles at [0, 2*TILE), V^T tiles at [2*TILE, 4*TILE)
   __shared__ __attribute__((aligned(16))) char lds[4 * TILE];
-  __shared__ int16_t s_cols[2048];
+  __shared__ int16_t s_cols[kColChunk];
   __shared__ int s_item;
 
   const int tid = threadIdx.x;
@@ -205,22 +209,23 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_
     const int64_t bh = row / a.nB;
     const int qb = (int)(row - bh * a.nB);
     int cnt = a.nB;
+    const int16_t* cols = DENSE ? nullptr : a.col_idx + row * a.nB;
     if (!DENSE) {
-      // the count and the whole column row are read together (entries past
-      // the count are in bounds and never used), not one after the other
+      // the count and the first chunk of the column row are read together
+      // (entries past the count are in bounds and never used), not one after
+      // the other
       const int cnt_ld = a.row_count[row];
-      const int16_t* cols = a.col_idx + row * a.nB;
-      for (int t = tid; t < a.nB; t += NT) s_cols[t] = cols[t];
+      const int n0 = CHUNKED ? min(a.nB, kColChunk) : a.nB;
+      for (int t = tid; t < n0; t += NT) s_cols[t] = cols[t];
       cnt = __builtin_amdgcn_readfirstlane(cnt_ld);
       __syncthreads();
     }
     const int64_t nlast = a.N - (int64_t)(a.nB - 1) * BLK;  // real keys of the last block
-    int U = cnt * NSUB;
-    if (cnt > 0) {
-      const int lastcol = DENSE ? a.nB - 1 : (int)s_cols[cnt - 1];
-      if (lastcol == a.nB - 1) U -= NSUB - (int)((nlast + KT - 1) / KT);
-    }
-    U = __builtin_amdgcn_readfirstlane(U);
+    // the column list is walked in chunks of kColChunk held in s_cols (one
+    // chunk unless a row selects more blocks); U = sub-tiles of this chunk
+    int c0 = 0;
+    int ccnt = (DENSE || !CHUNKED) ? cnt : min(cnt, kColChunk);
+    int U = 0;
 
     // this head's K and V tiles (the tile of key0 starts at element key0*D)
     const __amdgpu_buffer_rsrc_t kbuf = byte_buffer(a.kr + bh * a.Npad * D, (int)(a.Npad * D * 2));
@@ -366,36 +371,52 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_
       }
     };
 
-    if (U > 0) {
-      // prologue: K(0), V(0), K(1) in flight; S(0) once K(0) has landed
-      load_k(0);
-      load_v(0);
-      if (U > 1) load_k(1);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      f32x16 sa[2][QT], sb[2][QT];
-      qk(0, sa);
-      // steady state: at iteration u, S(u) is in registers, K(u+1) and V(u)
-      // are (being) loaded; K(u+2) and V(u+1) are issued here.  S(u+1) is
-      // computed unconditionally (on a stale buffer after the last tile; the
-      // result is then unused) so the products of the next tile and the
-      // softmax of this one share one basic block.
-      auto step = [&](int u, f32x16 (&sc)[2][QT], f32x16 (&sn)[2][QT]) {
+    while (true) {
+      U = ccnt * NSUB;
+      if (ccnt > 0 && c0 + ccnt == cnt) {
+        const int lastcol = DENSE ? a.nB - 1 : (int)s_cols[ccnt - 1];
+        if (lastcol == a.nB - 1) U -= NSUB - (int)((nlast + KT - 1) / KT);
+      }
+      U = __builtin_amdgcn_readfirstlane(U);
+      if (U > 0) {
+        // prologue: K(0), V(0), K(1) in flight; S(0) once K(0) has landed
+        load_k(0);
+        load_v(0);
+        if (U > 1) load_k(1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (u + 2 < U) load_k(u + 2);
-        if (u + 1 < U) load_v(u + 1);
-        prep(u, sc);
-        bf16x8 pop[2][2][QT];
-        qk(u + 1, sn);
-        probs(sc, pop);
-        pv(u, pop);
-      };
-      for (int u = 0; u < U; u += 2) {
-        step(u, sa, sb);
-        if (u + 1 >= U) break;
-        step(u + 1, sb, sa);
+        f32x16 sa[2][QT], sb[2][QT];
+        qk(0, sa);
+        // steady state: at iteration u, S(u) is in registers, K(u+1) and V(u)
+        // are (being) loaded; K(u+2) and V(u+1) are issued here.  S(u+1) is
+        // computed unconditionally (on a stale buffer after the last tile; the
+        // result is then unused) so the products of the next tile and the
+        // softmax of this one share one basic block.
+        auto step = [&](int u, f32x16 (&sc)[2][QT], f32x16 (&sn)[2][QT]) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          if (u + 2 < U) load_k(u + 2);
+          if (u + 1 < U) load_v(u + 1);
+          prep(u, sc);
+          bf16x8 pop[2][2][QT];
+          qk(u + 1, sn);
+          probs(sc, pop);
+          pv(u, pop);
+        };
+        for (int u = 0; u < U; u += 2) {
+          step(u, sa, sb);
+          if (u + 1 >= U) break;
+          step(u + 1, sb, sa);
+        }
       }
+      c0 += ccnt;
+      if (DENSE || !CHUNKED || c0 >= cnt) break;
+      // next chunk of the column list: every wave is done with the tile
+      // buffers and the previous chunk before either is overwritten
+      __syncthreads();
+      ccnt = min(cnt - c0, kColChunk);
+      for (int t = tid; t < ccnt; t += NT) s_cols[t] = cols[c0 + t];
+      __syncthreads();
     }
 
     // finalize: total sum over both half-waves, normalize, write bf16
@@ -512,16 +533,11 @@ __global__ __launch_bounds__(kPlanThreads) void xcd_plan_kernel(const int32_t* h
 
 constexpr int kQT = 1;  // 32-query tiles per wave in the launched kernels
 
-template <int D, int BLK>
-fva_status launch_t(const Problem& p, AttnArgs a, int flags, bool dense, hipStream_t s) {
+template <int D, int BLK, bool CH>
+fva_status launch_sparse(const Problem& p, AttnArgs a, int flags, hipStream_t s) {
   const int sched = flags & 0x3;
   const bool trace = (flags & FVA_TRACE) != 0;
   constexpr int NT = attn_threads<kQT>(BLK);
-  if (dense) {
-    hipLaunchKernelGGL((attn_kernel<D, BLK, kQT, FVA_SCHED_GRID, true, false>), dim3((unsigned)p.rows),
-                       dim3(NT), 0, s, a);
-    return hip_fail(hipGetLastError(), "dense attention launch");
-  }
   // persistent grid: as many workgroups as can be resident at once (the
   // occupancy query costs microseconds of host time, so it is asked once per
   // device and kept)
@@ -533,7 +549,7 @@ fva_status launch_t(const Problem& p, AttnArgs a, int flags, bool dense, hipStre
   int per_cu = (dev >= 0 && dev < 64) ? __atomic_load_n(&occ_cache[dev], __ATOMIC_ACQUIRE) : 0;
   if (per_cu == 0) {
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, reinterpret_cast<const void*>(&attn_kernel<D, BLK, kQT, FVA_SCHED_QUEUE, false, false>),
+        &per_cu, reinterpret_cast<const void*>(&attn_kernel<D, BLK, kQT, FVA_SCHED_QUEUE, false, false, CH>),
         NT, 0);
     if (e != hipSuccess) return hip_fail(e, "occupancy query");
     if (per_cu < 1) per_cu = 1;
@@ -542,7 +558,7 @@ fva_status launch_t(const Problem& p, AttnArgs a, int flags, bool dense, hipStre
   const int64_t slots = (int64_t)cus * per_cu;
   const int64_t persist = std::min<int64_t>(p.rows, slots);
 #define FVA_LAUNCH(SCH, TR, GRIDN)                                                         \
-  hipLaunchKernelGGL((attn_kernel<D, BLK, kQT, SCH, false, TR>), dim3((unsigned)(GRIDN)), dim3(NT), \
+  hipLaunchKernelGGL((attn_kernel<D, BLK, kQT, SCH, false, TR, CH>), dim3((unsigned)(GRIDN)), dim3(NT), \
                      0, s, a)
   // When every item fits in one wave of resident workgroups, each persistent
   // workgroup of the queue and XCD schedules would run exactly one item: one
@@ -573,6 +589,18 @@ fva_status launch_t(const Problem& p, AttnArgs a, int flags, bool dense, hipStre
   }
 #undef FVA_LAUNCH
   return hip_fail(hipGetLastError(), "sparse attention launch");
+}
+
+template <int D, int BLK>
+fva_status launch_t(const Problem& p, AttnArgs a, int flags, bool dense, hipStream_t s) {
+  if (dense) {
+    constexpr int NT = attn_threads<kQT>(BLK);
+    hipLaunchKernelGGL((attn_kernel<D, BLK, kQT, FVA_SCHED_GRID, true, false, false>),
+                       dim3((unsigned)p.rows), dim3(NT), 0, s, a);
+    return hip_fail(hipGetLastError(), "dense attention launch");
+  }
+  return p.nB > kColChunk ? launch_sparse<D, BLK, true>(p, a, flags, s)
+                          : launch_sparse<D, BLK, false>(p, a, flags, s);
 }
 
 // Attention workspace for callers that cannot allocate: every device that

@@ -37,7 +37,9 @@ fva_status make_problem(const fva_grid* g, int32_t B, int32_t Hh, int32_t d, Pro
     return fail(FVA_ERR_UNSUPPORTED, "block size %lld not in {64,128}", (long long)BLK);
   const int64_t N = (int64_t)g->T * g->H * g->W;
   const int64_t nB = (N + BLK - 1) / BLK;
-  if (nB > 2048) return fail(FVA_ERR_UNSUPPORTED, "%lld blocks exceed 2048", (long long)nB);
+  if (nB > 32767)
+    return fail(FVA_ERR_UNSUPPORTED, "%lld blocks exceed 32767 (int16 column indices)",
+                (long long)nB);
   const int64_t rows = (int64_t)B * Hh * nB;
   if (rows >= (1ll << 31)) return fail(FVA_ERR_UNSUPPORTED, "too many rows");
   p->B = B;

@@ -178,20 +178,20 @@ __device__ void bitonic_sort(K* keys, int P) {
 template <int NT>
 __device__ void emit_row(const uint32_t* bits, int words, uint32_t* bm_out, int16_t* col_out,
                          int* wpre) {
-  if (threadIdx.x < words) {
-    bm_out[threadIdx.x] = bits[threadIdx.x];
+  for (int w = threadIdx.x; w < words; w += NT) {
+    bm_out[w] = bits[w];
     int pre = 0;
-    for (int w = 0; w < (int)threadIdx.x; ++w) pre += __popc(bits[w]);
-    wpre[threadIdx.x] = pre;
+    for (int v = 0; v < w; ++v) pre += __popc(bits[v]);
+    wpre[w] = pre;
   }
   __syncthreads();
-  if (threadIdx.x < words) {
-    uint32_t m = bits[threadIdx.x];
-    int pos = wpre[threadIdx.x];
+  for (int w = threadIdx.x; w < words; w += NT) {
+    uint32_t m = bits[w];
+    int pos = wpre[w];
     while (m) {
       const int bit = __ffs(m) - 1;
       m &= m - 1u;
-      col_out[pos++] = (int16_t)(threadIdx.x * 32 + bit);
+      col_out[pos++] = (int16_t)(w * 32 + bit);
     }
   }
 }
@@ -216,8 +216,9 @@ __device__ void emit_row(const uint32_t* bits, int words, uint32_t* bm_out, int1
 // ballot prefix counts place the ascending column list.
 constexpr int kRouteThreads = 256;
 constexpr int kRouteRowsPerBlock = kRouteThreads / 64;
-constexpr int kMaxNB = 2048;
+constexpr int kMaxWaveNB = 2048;  // rows up to this many blocks: one wave per row
 constexpr int kKeyBits = 43;
+constexpr int kMaxNB = 32767;     // int16 column indices
 
 // Sum of a double over the wave, the same bits in every lane.  Each step adds
 // a partner lane's value with DPP or a lane swap (no LDS traffic): mirror
@@ -375,6 +376,180 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   }
 }
 
+// Rows of more than kMaxWaveNB blocks: one 1024-thread workgroup per row, the
+// same threshold searches over 47-bit keys (order_key(s) << 15 | (32767 - j)),
+// with every wave total combined across the 16 waves through LDS in wave
+// order, so the sums stay deterministic.  Thread t holds blocks t + 1024e; it
+// keeps the 32-bit order keys and the float64 exponentials in registers and
+// forms the full key when it compares (past 8 blocks per thread, E = 16 and
+// 32, part of them lives in scratch memory: slower, same results).
+constexpr int kWideThreads = 1024;
+constexpr int kWideWaves = kWideThreads / 64;
+constexpr int kWideKeyBits = 47;
+
+template <int E>
+__global__ __launch_bounds__(kWideThreads) void route_wide_kernel(
+    const float* __restrict__ S, int nB, int words, float top_p, int topk,
+    uint32_t* __restrict__ bitmask, int32_t* __restrict__ row_count,
+    int16_t* __restrict__ col_idx, int32_t* __restrict__ head_count, uint32_t* flags) {
+  __shared__ double dred[2][kWideWaves];
+  __shared__ int ired[2][kWideWaves];
+  __shared__ float fred[kWideWaves];
+  __shared__ uint64_t s_only;
+  __shared__ int wbase[32 * kWideWaves];  // selected counts per (e, wave), then their exclusive prefix
+  __shared__ int wtot[kWideWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = blockIdx.x;
+  const int64_t bh = row / nB;
+  const float* s = S + row * nB;
+  uint32_t ok[E];  // order keys; slots past nB are not keys (key_of gives 0)
+  bool nan_seen = false;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = threadIdx.x + kWideThreads * e;
+    ok[e] = 0u;
+    if (j < nB) {
+      const float x = s[j];
+      nan_seen |= (x != x);
+      ok[e] = order_key(x);
+      mx = fmaxf(mx, x);
+    }
+  }
+  auto key_of = [&](int e) -> uint64_t {
+    const int j = threadIdx.x + kWideThreads * e;
+    return j < nB ? ((uint64_t)ok[e] << 15) | (uint64_t)(32767 - j) : 0ull;
+  };
+  if (__builtin_amdgcn_ballot_w64(nan_seen) && lane == 0) atomicOr(flags, 1u);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if (lane == 0) fred[wave] = mx;
+  __syncthreads();
+  mx = fred[0];
+  for (int w = 1; w < kWideWaves; ++w) mx = fmaxf(mx, fred[w]);
+
+  // block totals: each wave's total (identical in its lanes) is combined in
+  // wave order; two alternating buffers let one barrier serve each total
+  int ph = 0;
+  auto block_sum_f64 = [&](double wave_total) -> double {
+    if (lane == 0) dred[ph][wave] = wave_total;
+    __syncthreads();
+    double t = 0.0;
+    for (int w = 0; w < kWideWaves; ++w) t += dred[ph][w];
+    ph ^= 1;
+    return t;
+  };
+  auto block_sum_i32 = [&](int wave_total) -> int {
+    if (lane == 0) ired[ph][wave] = wave_total;
+    __syncthreads();
+    int t = 0;
+    for (int w = 0; w < kWideWaves; ++w) t += ired[ph][w];
+    ph ^= 1;
+    return t;
+  };
+  auto count_ge = [&](uint64_t x) -> int {
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(key_of(e) >= x));
+    return block_sum_i32(c);
+  };
+
+  uint64_t thr;
+  if (top_p >= 1.0f) {
+    thr = 1;
+  } else if (top_p <= 0.0f) {
+    thr = ~0ull;
+  } else {
+    const double m = (double)mx;
+    double ev[E];
+    double part = 0.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      ev[e] = key_of(e) != 0 ? exp((double)order_key_inv(ok[e]) - m) : 0.0;
+      part += ev[e];
+    }
+    const double target = (double)top_p * block_sum_f64(wave_sum_f64(part));
+    auto search = [&](uint64_t x, int hi_bit, int lo_bit) {
+      for (int b = hi_bit; b >= lo_bit; --b) {
+        const uint64_t c = x | (1ull << b);
+        double t = 0.0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) t += key_of(e) >= c ? ev[e] : 0.0;
+        if (block_sum_f64(wave_sum_f64(t)) >= target) x = c;
+      }
+      return x;
+    };
+    uint64_t x = search(0, kWideKeyBits - 1, 15);
+    int ties = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint64_t k = key_of(e);
+      const bool tie = k != 0 && (k >> 15) == (x >> 15);
+      if (tie) s_only = k;  // read only when exactly one key ties
+      ties += __builtin_popcountll(__builtin_amdgcn_ballot_w64(tie));
+    }
+    ties = block_sum_i32(ties);  // its barrier also publishes s_only
+    thr = ties == 1 ? s_only : search(x, 14, 0);
+  }
+  if (topk > 0 && count_ge(thr) < topk) {
+    if (topk >= nB) {
+      thr = 1;
+    } else {
+      uint64_t x = 0;
+      for (int b = kWideKeyBits - 1; b >= 0; --b) {
+        const uint64_t c = x | (1ull << b);
+        if (count_ge(c) >= topk) x = c;
+      }
+      thr = x;
+    }
+  }
+
+  // bitmask words straight from the ballots; the column list from an
+  // exclusive scan of the per-(e, wave) counts in block order (e major)
+  uint32_t* bm = bitmask + row * words;
+  int16_t* ci = col_idx + row * nB;
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint64_t k = key_of(e);
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(k != 0 && k >= thr);
+    const int w0 = 32 * e + 2 * wave;
+    if (lane < 2 && w0 + lane < words) bm[w0 + lane] = (uint32_t)(bal >> (32 * lane));
+    if (lane == 0) wbase[e * kWideWaves + wave] = __builtin_popcountll(bal);
+  }
+  __syncthreads();
+  const int f = threadIdx.x;  // E*16 <= 512 entries: waves 0..7 hold them
+  const int v = f < E * kWideWaves ? wbase[f] : 0;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();  // also: every thread has read its wbase entry
+  int before = 0, mine = 0;
+  for (int w = 0; w < kWideWaves; ++w) {
+    if (w < wave) before += wtot[w];
+    mine += wtot[w];
+  }
+  if (f < E * kWideWaves) wbase[f] = before + incl - v;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint64_t k = key_of(e);
+    const bool sel = k != 0 && k >= thr;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(sel);
+    if (sel)
+      ci[wbase[e * kWideWaves + wave] + __builtin_popcountll(bal & below)] =
+          (int16_t)(threadIdx.x + kWideThreads * e);
+  }
+  if (threadIdx.x == 0) {
+    row_count[row] = mine;
+    atomicAdd(&head_count[bh], mine);
+  }
+}
+
 // ------------------------------------------------------------------ top-up
 // Priority key of pair (i, j) with score s: smaller = higher priority
 // (score descending, then i ascending, then j ascending).  62 bits.
@@ -467,9 +642,9 @@ __global__ __launch_bounds__(kRouteThreads) void topup_apply_kernel(
     const float* __restrict__ S, int nB, int words, const uint64_t* __restrict__ thresh,
     uint32_t* __restrict__ bitmask, int32_t* __restrict__ row_count,
     int16_t* __restrict__ col_idx, int32_t* __restrict__ head_count) {
-  __shared__ uint32_t bits[kMaxNB / 32];
+  __shared__ uint32_t bits[(kMaxNB + 31) / 32];
   __shared__ int red[4];
-  __shared__ int wpre[kMaxNB / 32];
+  __shared__ int wpre[(kMaxNB + 31) / 32];
   const int64_t row = blockIdx.x;
   const int64_t bh = row / nB;
   const int i = (int)(row - bh * nB);
@@ -510,11 +685,12 @@ __global__ __launch_bounds__(kQThreads) void queue_chunk_kernel(
     const int32_t* __restrict__ row_count, int64_t rows, int nB, int32_t* __restrict__ tmp_row,
     int32_t* __restrict__ tmp_rank, int32_t* __restrict__ hist) {
   __shared__ uint32_t keys[kQThreads];
-  __shared__ int32_t lhist[kMaxNB + 1];
   __shared__ int32_t wtot[kQThreads / 64];
   const int64_t base = (int64_t)blockIdx.x * kQThreads;
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-  for (int c = threadIdx.x; c <= nB; c += kQThreads) lhist[c] = 0;
+  // this chunk's run lengths by count (nB + 1 entries), zero where no row has it
+  int32_t* h = hist + (int64_t)blockIdx.x * (nB + 1);
+  for (int c = threadIdx.x; c <= nB; c += kQThreads) h[c] = 0;
   const int64_t item = base + threadIdx.x;
   keys[threadIdx.x] = item < rows
                           ? ((uint32_t)(nB - row_count[item]) << 10) | (uint32_t)threadIdx.x
@@ -545,11 +721,8 @@ __global__ __launch_bounds__(kQThreads) void queue_chunk_kernel(
     tmp_row[base + threadIdx.x] = (int32_t)(base + (k & 1023u));
     tmp_rank[base + threadIdx.x] = (int)threadIdx.x - st;
     const bool tail = threadIdx.x == kQThreads - 1 || (keys[threadIdx.x + 1] >> 10) != grp;
-    if (tail) lhist[nB - (int)grp] = (int)threadIdx.x - st + 1;
+    if (tail) h[nB - (int)grp] = (int)threadIdx.x - st + 1;
   }
-  __syncthreads();
-  int32_t* h = hist + (int64_t)blockIdx.x * (nB + 1);
-  for (int c = threadIdx.x; c <= nB; c += kQThreads) h[c] = lhist[c];
 }
 
 // In-place exclusive scan of hist[chunk][c] in the order (c descending,
@@ -677,8 +850,18 @@ fva_status launch_route(const Problem& p, const void* qr, const void* kr,
                                                       kRouteRowsPerBlock)),                    \
                      dim3(kRouteThreads), 0, s, m.scores, p.nB, p.words, p.rows, prm.top_p,     \
                      prm.topk_floor, m.bitmask, m.row_count, m.col_idx, m.head_count, wflags)
+#define FVA_ROUTE_WIDE(E)                                                                      \
+  hipLaunchKernelGGL(route_wide_kernel<E>, dim3((unsigned)p.rows), dim3(kWideThreads), 0, s,   \
+                     m.scores, p.nB, p.words, prm.top_p, prm.topk_floor, m.bitmask,          \
+                     m.row_count, m.col_idx, m.head_count, wflags)
   const int per_lane = (p.nB + 63) / 64;
-  if (per_lane <= 2) FVA_ROUTE(2);
+  const int per_thread = (p.nB + kWideThreads - 1) / kWideThreads;
+  if (p.nB > kMaxWaveNB) {
+    if (per_thread <= 4) FVA_ROUTE_WIDE(4);
+    else if (per_thread <= 8) FVA_ROUTE_WIDE(8);
+    else if (per_thread <= 16) FVA_ROUTE_WIDE(16);
+    else FVA_ROUTE_WIDE(32);
+  } else if (per_lane <= 2) FVA_ROUTE(2);
   else if (per_lane <= 4) FVA_ROUTE(4);
   else if (per_lane <= 8) FVA_ROUTE(8);
   else if (per_lane <= 10) FVA_ROUTE(10);
@@ -687,6 +870,7 @@ fva_status launch_route(const Problem& p, const void* qr, const void* kr,
   else if (per_lane <= 24) FVA_ROUTE(24);
   else FVA_ROUTE(32);
 #undef FVA_ROUTE
+#undef FVA_ROUTE_WIDE
   if (prm.aug_budget > 0) launch_topup_kernels(p, m, ws, (int64_t)prm.aug_budget, nullptr, s);
   launch_queue(p, m, ws, s);
   return hip_fail(hipGetLastError(), "route launch");

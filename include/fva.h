@@ -25,8 +25,8 @@
  *     thread-local message.  Nothing is launched when validation fails.
  *   - bf16 tensors are IEEE bfloat16 stored as uint16.
  *   - Supported: head dim d in {64, 128}; block size BLK = bt*bh*bw in
- *     {64, 128}; number of blocks nB <= 2048; B*Hh*nB < 2^31.  Other shapes
- *     return FVA_ERR_UNSUPPORTED.
+ *     {64, 128}; number of blocks nB <= 32767 (int16 column indices);
+ *     B*Hh*nB < 2^31.  Other shapes return FVA_ERR_UNSUPPORTED.
  *   - Calls are reentrant (no global mutable state) apart from the per-thread
  *     error string.
  *

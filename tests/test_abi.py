@@ -56,8 +56,12 @@ def test_validation_errors_before_launch(lib):
     assert lib.fva_sizes(ctypes.byref(bad), 1, 2, 64, ctypes.byref(out)) == F.FVA_ERR_UNSUPPORTED
     neg = F.make_grid((0, 16, 16), (1, 8, 8))
     assert lib.fva_sizes(ctypes.byref(neg), 1, 2, 64, ctypes.byref(out)) == F.FVA_ERR_INVALID_ARG
-    big = F.make_grid((64, 64, 64), (1, 8, 8))      # 4096 blocks
+    big = F.make_grid((64, 256, 128), (1, 8, 8))    # 32768 blocks: past int16 column indices
     assert lib.fva_sizes(ctypes.byref(big), 1, 2, 64, ctypes.byref(out)) == F.FVA_ERR_UNSUPPORTED
+    assert b"32767" in lib.fva_last_error()
+    most = F.make_grid((1, 1, 32767 * 64), (1, 1, 64))  # the largest block count
+    assert lib.fva_sizes(ctypes.byref(most), 1, 2, 64, ctypes.byref(out)) == F.FVA_OK
+    assert out.nB == 32767 and out.words == 1024
     st = (ctypes.c_int64 * 3)(1280 * 2 * 64, 2 * 64, 64)
     # null pointers
     assert lib.fva_reorder(None, None, 1, 2, 64, ctypes.byref(g), st, 0, 0, None) == \

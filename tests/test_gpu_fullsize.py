@@ -168,6 +168,7 @@ def run_case(w, n_random=12):
         e_rec = max(e_rec, float(np.abs(rec - O.mask_recall(ref_s, ref_d)).max()))
     print(f"[{w.name}] lse max_abs={e_lse:.2e} recall max_abs={e_rec:.2e}", flush=True)
     assert e_lse <= LSE_ABS and e_rec <= RECALL_ABS
+    return r
 
 
 @pytest.mark.parametrize("name", ["480p", "720p", "hetero", "long720p"])
@@ -180,3 +181,58 @@ def test_largest_supported_block_count():
     w = small_workload("max-nB", 2, 64, (16, 128, 128), (1, 8, 16), 0.9, 4, aug_budget=300000)
     assert w.nB == 2048
     run_case(w, n_random=6)
+
+
+def test_rows_of_more_than_2048_blocks():
+    # nB = 4100: routing takes one 1024-thread workgroup per row (four blocks
+    # per thread); the near-uniform head keeps about 90 % of the blocks, so
+    # attention walks column lists of more than 2048 entries in LDS chunks;
+    # the top-up rewrites rows of 129 bitmask words
+    w = small_workload("wide-nB", 2, 64, (4, 64, 1025), (1, 8, 8), 0.9, 4,
+                       aug_budget=int(0.3 * 4100 * 4100), amp=(0.2, 3.0))
+    assert w.nB == 4100
+    r = run_case(w, n_random=6)
+    counts = r["counts"].reshape(-1)
+    assert counts.max() > 2048 and counts.min() < 2048
+
+
+@pytest.mark.parametrize("top_p,topk", [(0.9, 4), (0.0, 5000), (1.0, 0), (0.5, 9000)])
+def test_route_of_the_widest_rows_sampled(top_p, topk):
+    # nB = 17000 (16 or more blocks per thread of the row's workgroup): route
+    # from seeded float32 scores with many ties and signed zeros; sampled rows
+    # bit for bit against the oracle, every count and W_h, a valid queue
+    grid = F.make_grid((1, 1, 17000 * 64), (1, 1, 64))
+    sz = F.fva_sizes(grid, 1, 1, 64)
+    nB, rows = int(sz.nB), int(sz.rows)
+    assert nB == 17000
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    S = torch.randn((rows, nB), device="cuda", generator=gen) * 4.0
+    S = torch.round(S * 16.0) / 16.0                   # many ties
+    S[S == 0] = -0.0                                    # signed zeros among them
+    S[::7, ::5] = 0.0
+    bitmask = torch.empty((rows, int(sz.words)), dtype=torch.int32, device="cuda")
+    row_count = torch.empty(rows, dtype=torch.int32, device="cuda")
+    col_idx = torch.empty((rows, nB), dtype=torch.int16, device="cuda")
+    head_count = torch.empty(1, dtype=torch.int32, device="cuda")
+    queue = torch.empty(rows, dtype=torch.int32, device="cuda")
+    ws = torch.zeros((int(sz.route_ws_bytes) + 7) // 8, dtype=torch.int64, device="cuda")
+    m = F.fva_mask(S.data_ptr(), bitmask.data_ptr(), row_count.data_ptr(), col_idx.data_ptr(),
+                   head_count.data_ptr(), queue.data_ptr())
+    prm = F.fva_route_params(top_p, topk, 0, 0.0, 0)
+    F.fva_route(None, None, 1, 1, 64, grid, prm, m, ws, int(sz.route_ws_bytes),
+                F.FVA_ROUTE_SCORES_IN)
+    torch.cuda.synchronize()
+    rc = row_count.cpu().numpy()
+    assert int(head_count.item()) == int(rc.sum())
+    q = queue.cpu().numpy()
+    assert np.array_equal(np.sort(q), np.arange(rows))
+    assert np.array_equal(q, O.heaviest_first(rc.reshape(1, 1, -1).astype(np.int64)))
+    sample = np.random.default_rng(3).choice(rows, size=24, replace=False)
+    S32 = S[torch.from_numpy(sample).cuda()].cpu().numpy()
+    mask, counts, _ = O.route(S32, top_p, topk)
+    got = unpack_bitmask(bitmask[torch.from_numpy(sample).cuda()], nB)
+    assert np.array_equal(got, mask)
+    assert np.array_equal(rc[sample], counts)
+    ci = col_idx[torch.from_numpy(sample).cuda()].cpu().numpy()
+    for k in range(len(sample)):
+        assert np.array_equal(ci[k, :counts[k]], np.nonzero(mask[k])[0])
