@@ -127,18 +127,26 @@ def cpu_baseline(w, q, k, v, seconds):
     t1 = time.perf_counter()
     r = O.route_path(qr, kr, w.N, w.BLK, w.scale, w.top_p, w.topk_floor, w.aug_budget)
     t2 = time.perf_counter()
+    # a stated head subset: the lightest and the heaviest head by W_h and two
+    # seeded others; their query blocks are taken round-robin across the four
+    # heads, each head's in seeded order, until the time budget is spent
     rng = np.random.default_rng(0)
-    items = rng.permutation(w.B * w.Hh * w.nB)
+    hc = r["head_count"].reshape(-1)
+    light, heavy = int(np.argmin(hc)), int(np.argmax(hc))
+    others = [x for x in rng.permutation(hc.shape[0]).tolist() if x not in (light, heavy)][:2]
+    heads = [light, heavy] + others
+    orders = [rng.permutation(w.nB) for _ in heads]
     counts = r["counts"].reshape(-1)
     flops, n = 0.0, 0
     ts = time.perf_counter()
-    for it in items:
-        b, rem = divmod(int(it), w.Hh * w.nB)
-        h, i = divmod(rem, w.nB)
-        O.sparse_attention(qr, kr, vr, r["mask"], w.N, w.BLK, w.scale, items=[(b, h, i)])
-        flops += 4.0 * w.d * w.BLK * w.BLK * counts[it]
-        n += 1
-        if time.perf_counter() - ts >= seconds and n >= 4:
+    for step in range(w.nB):
+        for bh, order in zip(heads, orders):
+            b, h = divmod(bh, w.Hh)
+            i = int(order[step])
+            O.sparse_attention(qr, kr, vr, r["mask"], w.N, w.BLK, w.scale, items=[(b, h, i)])
+            flops += 4.0 * w.d * w.BLK * w.BLK * counts[bh * w.nB + i]
+            n += 1
+        if time.perf_counter() - ts >= seconds:
             break
     dt = time.perf_counter() - ts
     cpu_model = "unknown"
@@ -153,10 +161,12 @@ def cpu_baseline(w, q, k, v, seconds):
     return {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
         "cpu_model": cpu_model,
-        "sample": (f"float64 numpy oracle, attention of {n} seeded-random (head, query-block) "
-                   f"items of the {w.name} workload ({flops / 1e12:.3f} executed TFLOP in "
-                   f"{dt:.1f} s); its reorder of Q,K,V took {t1 - t0:.1f} s and routing of all "
-                   f"{w.B * w.Hh * w.nB} rows {t2 - t1:.1f} s (not in value)"),
+        "sample": (f"float64 numpy oracle, attention of {n} (head, query-block) items of the "
+                   f"{w.name} workload from heads {heads} (lightest and heaviest by W_h, up to two "
+                   f"seeded), round-robin over the heads in seeded query-block order "
+                   f"({flops / 1e12:.3f} executed TFLOP in {dt:.1f} s); its reorder of Q,K,V took "
+                   f"{t1 - t0:.1f} s and routing of all {w.B * w.Hh * w.nB} rows {t2 - t1:.1f} s "
+                   f"(not in value); cores = the BLAS threads its matrix products ran on"),
         "route_density": float(r["head_count"].sum() / (w.B * w.Hh * w.nB ** 2)),
     }
 
