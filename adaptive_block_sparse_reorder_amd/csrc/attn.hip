@@ -120,14 +120,26 @@ struct AttnArgs {
 template <int QT>
 constexpr int attn_threads(int blk) { return blk / (32 * QT) * 64; }
 
+// Teams per workgroup when a launch has no more rows than CUs: each team
+// (BLK/32 waves, its own K/V double buffers) walks every TEAMS-th key
+// sub-tile of the row and the teams' softmax states are merged in LDS at the
+// end, so a row's critical path is shared.  At most two waves per SIMD and
+// 128 KB of tile buffers per workgroup.
+template <int D, int BLK>
+constexpr int attn_teams() { return (D == 64 && BLK == 64) ? 4 : 2; }
+
 // CHUNKED: rows may select more than kColChunk blocks, so the column list
 // is walked in LDS chunks (launched only when nB > kColChunk; otherwise the
 // walk is one straight pass over a list read whole).
-template <int D, int BLK, int QT, int SCHED, bool DENSE, bool TRACE, bool CHUNKED>
-__global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_per_eu(
+// TEAMS: 1, or attn_teams<D, BLK>() for launches with rows <= CUs (never
+// together with CHUNKED).
+template <int D, int BLK, int QT, int SCHED, bool DENSE, bool TRACE, bool CHUNKED, int TEAMS>
+__global__ __launch_bounds__(attn_threads<QT>(BLK) * TEAMS) __attribute__((amdgpu_waves_per_eu(
     QT == 1 ? 2 : 1, QT == 1 ? 2 : 1))) void attn_kernel(AttnArgs a) {
-  constexpr int NT = attn_threads<QT>(BLK);  // threads: BLK/(32*QT) waves
+  static_assert(TEAMS == 1 || !CHUNKED, "teams serve short launches only");
+  constexpr int NT = attn_threads<QT>(BLK);  // threads of one team: BLK/(32*QT) waves
   constexpr int NW = NT / 64;
+  constexpr int NTALL = NT * TEAMS;          // threads of the workgroup
   constexpr int TILE = KT * D * 2;       // bytes of one K or V^T sub-tile
   constexpr int NSUB = BLK / KT;         // sub-tiles per key block
   constexpr int KSTEPS = D / 16;         // MFMA k-steps over the head dim
@@ -135,14 +147,17 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_
   constexpr int CPR = D / 8;             // 16-byte chunks per K row
   constexpr int LOADS = TILE / 16 / NT;  // 16-byte loads per thread per K (or V) tile
   static_assert(LOADS * 16 * NT == TILE, "tile size");
-  // LDS: K tiles at [0, 2*TILE), V^T tiles at [2*TILE, 4*TILE)
-  __shared__ __attribute__((aligned(16))) char lds[4 * TILE];
+  // LDS per team: K tiles at [0, 2*TILE), V^T tiles at [2*TILE, 4*TILE)
+  __shared__ __attribute__((aligned(16))) char lds_all[4 * TILE * TEAMS];
   __shared__ int16_t s_cols[kColChunk];
   __shared__ int s_item;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int team = TEAMS == 1 ? 0 : __builtin_amdgcn_readfirstlane((tid >> 6) / NW);
+  const int wave = TEAMS == 1 ? __builtin_amdgcn_readfirstlane(tid >> 6)
+                              : __builtin_amdgcn_readfirstlane((tid >> 6) % NW);  // in its team
+  char* const lds = lds_all + team * 4 * TILE;
   const int l32 = lane & 31;
   const int hl = lane >> 5;
 
@@ -208,6 +223,16 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_
     row = __builtin_amdgcn_readfirstlane((int)row);
     const int64_t bh = row / a.nB;
     const int qb = (int)(row - bh * a.nB);
+    // Q^T operands: q-tile j of this wave = 32 queries; lane holds query l32,
+    // d chunk 2kk+hl (issued first: their latency overlaps the column list's)
+    const int64_t q0 = (int64_t)qb * BLK + wave * 32 * QT;
+    bf16x8 qop[QT][KSTEPS];
+#pragma unroll
+    for (int j = 0; j < QT; ++j) {
+      const uint16_t* qp = a.qr + (bh * a.Npad + q0 + 32 * j + l32) * D + hl * 8;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) qop[j][kk] = as_bf16x8(*(const u32x4*)(qp + kk * 16));
+    }
     int cnt = a.nB;
     const int16_t* cols = DENSE ? nullptr : a.col_idx + row * a.nB;
     if (!DENSE) {
@@ -216,7 +241,7 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_
       // the other
       const int cnt_ld = a.row_count[row];
       const int n0 = CHUNKED ? min(a.nB, kColChunk) : a.nB;
-      for (int t = tid; t < n0; t += NT) s_cols[t] = cols[t];
+      for (int t = tid; t < n0; t += NTALL) s_cols[t] = cols[t];
       cnt = __builtin_amdgcn_readfirstlane(cnt_ld);
       __syncthreads();
     }
@@ -242,18 +267,11 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_
       for (int k = 0; k < LOADS; ++k)
         buf2lds16(rs, loff, soff + k * NW * 1024, buf + (k * NW + wave) * 1024);
     };
-    auto load_k = [&](int u) { load_tile(kbuf, u, lds + (u & 1) * TILE); };
-    auto load_v = [&](int u) { load_tile(vbuf, u, lds + (2 + (u & 1)) * TILE); };
-
-    // Q^T operands: q-tile j of this wave = 32 queries; lane holds query l32, d chunk 2kk+hl
-    const int64_t q0 = (int64_t)qb * BLK + wave * 32 * QT;
-    bf16x8 qop[QT][KSTEPS];
-#pragma unroll
-    for (int j = 0; j < QT; ++j) {
-      const uint16_t* qp = a.qr + (bh * a.Npad + q0 + 32 * j + l32) * D + hl * 8;
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) qop[j][kk] = as_bf16x8(*(const u32x4*)(qp + kk * 16));
-    }
+    // team-local sub-tile v is the row's sub-tile team + v*TEAMS; the local
+    // index picks the buffer, the row's index the keys
+    auto gsub = [&](int v) { return TEAMS == 1 ? v : team + v * TEAMS; };
+    auto load_k = [&](int u) { load_tile(kbuf, gsub(u), lds + (u & 1) * TILE); };
+    auto load_v = [&](int u) { load_tile(vbuf, gsub(u), lds + (2 + (u & 1)) * TILE); };
 
     f32x16 oacc[DT][QT];
 #pragma unroll
@@ -287,7 +305,7 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_
     };
     // masking of padded keys, tile max and lazy rescale for sub-tile u
     auto prep = [&](int u, f32x16 (&s)[2][QT]) {
-      const int kvalid = (int)min((int64_t)KT, a.N - key0_of(u));
+      const int kvalid = (int)min((int64_t)KT, a.N - key0_of(gsub(u)));
       if (kvalid < KT) {
 #pragma unroll
         for (int m = 0; m < 2; ++m)
@@ -378,15 +396,21 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_
         if (lastcol == a.nB - 1) U -= NSUB - (int)((nlast + KT - 1) / KT);
       }
       U = __builtin_amdgcn_readfirstlane(U);
-      if (U > 0) {
+      // this team's sub-tiles, and the steps every team takes (the teams
+      // share the per-step barrier; a team past its last sub-tile idles)
+      const int Ut = TEAMS == 1 ? U : (U > team ? (U - 1 - team) / TEAMS + 1 : 0);
+      const int S = TEAMS == 1 ? U : (U + TEAMS - 1) / TEAMS;
+      if (S > 0) {
         // prologue: K(0), V(0), K(1) in flight; S(0) once K(0) has landed
-        load_k(0);
-        load_v(0);
-        if (U > 1) load_k(1);
+        if (TEAMS == 1 || Ut > 0) {
+          load_k(0);
+          load_v(0);
+        }
+        if (Ut > 1) load_k(1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         f32x16 sa[2][QT], sb[2][QT];
-        qk(0, sa);
+        if (TEAMS == 1 || Ut > 0) qk(0, sa);
         // steady state: at iteration u, S(u) is in registers, K(u+1) and V(u)
         // are (being) loaded; K(u+2) and V(u+1) are issued here.  S(u+1) is
         // computed unconditionally (on a stale buffer after the last tile; the
@@ -395,17 +419,19 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_
         auto step = [&](int u, f32x16 (&sc)[2][QT], f32x16 (&sn)[2][QT]) {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           __syncthreads();
-          if (u + 2 < U) load_k(u + 2);
-          if (u + 1 < U) load_v(u + 1);
-          prep(u, sc);
-          bf16x8 pop[2][2][QT];
-          qk(u + 1, sn);
-          probs(sc, pop);
-          pv(u, pop);
+          if (u + 2 < Ut) load_k(u + 2);
+          if (u + 1 < Ut) load_v(u + 1);
+          if (TEAMS == 1 || u < Ut) {
+            prep(u, sc);
+            bf16x8 pop[2][2][QT];
+            qk(u + 1, sn);
+            probs(sc, pop);
+            pv(u, pop);
+          }
         };
-        for (int u = 0; u < U; u += 2) {
+        for (int u = 0; u < S; u += 2) {
           step(u, sa, sb);
-          if (u + 1 >= U) break;
+          if (u + 1 >= S) break;
           step(u + 1, sb, sa);
         }
       }
@@ -415,13 +441,53 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK)) __attribute__((amdgpu_waves_
       // buffers and the previous chunk before either is overwritten
       __syncthreads();
       ccnt = min(cnt - c0, kColChunk);
-      for (int t = tid; t < ccnt; t += NT) s_cols[t] = cols[c0 + t];
+      for (int t = tid; t < ccnt; t += NTALL) s_cols[t] = cols[c0 + t];
       __syncthreads();
     }
 
-    // finalize: total sum over both half-waves, normalize, write bf16
+    if (TEAMS > 1) {
+      // merge the teams' softmax states into team 0, team by team in order:
+      // with m = max of the references, O and l of each team scale by
+      // 2^(m_t - m) (0 for a team that saw no key)
+      static_assert(QT == 1, "teams merge one query tile per wave");
+      constexpr int PER = 2 + DT * 16;  // floats per lane: reference, sum, O
+      constexpr int SLOTS = NW * 64;    // lanes of one team
+      static_assert((TEAMS - 1) * PER * SLOTS * 4 <= 4 * TILE * TEAMS, "merge buffer");
+      float* const mb = reinterpret_cast<float*>(lds_all);
+      const int slot = wave * 64 + lane;
+      __syncthreads();  // every team is done with its tile buffers
+      if (team > 0) {
+        float* dst = mb + (team - 1) * PER * SLOTS + slot;
+        dst[0] = m_use[0];
+        dst[SLOTS] = l_run[0];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dst[(2 + dt * 16 + r) * SLOTS] = oacc[dt][0][r];
+      }
+      __syncthreads();
+      if (team == 0) {
+        for (int t = 1; t < TEAMS; ++t) {
+          const float* src = mb + (t - 1) * PER * SLOTS + slot;
+          const float mt = src[0];
+          const float mx = fmaxf(m_use[0], mt);
+          const float a0 = m_use[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_use[0] - mx);
+          const float at = mt == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mt - mx);
+          l_run[0] = l_run[0] * a0 + src[SLOTS] * at;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              oacc[dt][0][r] = oacc[dt][0][r] * a0 + src[(2 + dt * 16 + r) * SLOTS] * at;
+          m_use[0] = mx;
+        }
+      }
+    }
+
+    // finalize (team 0): total sum over both half-waves, normalize, write bf16
 #pragma unroll
     for (int j = 0; j < QT; ++j) {
+      if (TEAMS > 1 && team != 0) break;
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run[j]),
                                                        __float_as_uint(l_run[j]), false, false);
       const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
@@ -549,7 +615,7 @@ fva_status launch_sparse(const Problem& p, AttnArgs a, int flags, hipStream_t s)
   int per_cu = (dev >= 0 && dev < 64) ? __atomic_load_n(&occ_cache[dev], __ATOMIC_ACQUIRE) : 0;
   if (per_cu == 0) {
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, reinterpret_cast<const void*>(&attn_kernel<D, BLK, kQT, FVA_SCHED_QUEUE, false, false, CH>),
+        &per_cu, reinterpret_cast<const void*>(&attn_kernel<D, BLK, kQT, FVA_SCHED_QUEUE, false, false, CH, 1>),
         NT, 0);
     if (e != hipSuccess) return hip_fail(e, "occupancy query");
     if (per_cu < 1) per_cu = 1;
@@ -558,8 +624,24 @@ fva_status launch_sparse(const Problem& p, AttnArgs a, int flags, hipStream_t s)
   const int64_t slots = (int64_t)cus * per_cu;
   const int64_t persist = std::min<int64_t>(p.rows, slots);
 #define FVA_LAUNCH(SCH, TR, GRIDN)                                                         \
-  hipLaunchKernelGGL((attn_kernel<D, BLK, kQT, SCH, false, TR, CH>), dim3((unsigned)(GRIDN)), dim3(NT), \
+  hipLaunchKernelGGL((attn_kernel<D, BLK, kQT, SCH, false, TR, CH, 1>), dim3((unsigned)(GRIDN)), dim3(NT), \
                      0, s, a)
+  // No more rows than CUs, under every schedule: one workgroup per row, with
+  // teams of waves sharing each row's key sub-tiles (a launch this short is
+  // bound by its longest row, not by the total work).
+  if constexpr (!CH) {
+    if (p.rows <= cus) {
+      constexpr int T = attn_teams<D, BLK>();
+      a.direct = 1;
+      if (trace)
+        hipLaunchKernelGGL((attn_kernel<D, BLK, kQT, FVA_SCHED_GRID, false, true, false, T>),
+                           dim3((unsigned)p.rows), dim3(NT * T), 0, s, a);
+      else
+        hipLaunchKernelGGL((attn_kernel<D, BLK, kQT, FVA_SCHED_GRID, false, false, false, T>),
+                           dim3((unsigned)p.rows), dim3(NT * T), 0, s, a);
+      return hip_fail(hipGetLastError(), "sparse attention launch");
+    }
+  }
   // When every item fits in one wave of resident workgroups, each persistent
   // workgroup of the queue and XCD schedules would run exactly one item: one
   // plain launch with workgroup i on row i does the same work without the
@@ -595,8 +677,13 @@ template <int D, int BLK>
 fva_status launch_t(const Problem& p, AttnArgs a, int flags, bool dense, hipStream_t s) {
   if (dense) {
     constexpr int NT = attn_threads<kQT>(BLK);
-    hipLaunchKernelGGL((attn_kernel<D, BLK, kQT, FVA_SCHED_GRID, true, false, false>),
-                       dim3((unsigned)p.rows), dim3(NT), 0, s, a);
+    constexpr int T = attn_teams<D, BLK>();
+    if (p.rows <= device_cu_count())  // as for the sparse kernel
+      hipLaunchKernelGGL((attn_kernel<D, BLK, kQT, FVA_SCHED_GRID, true, false, false, T>),
+                         dim3((unsigned)p.rows), dim3(NT * T), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_kernel<D, BLK, kQT, FVA_SCHED_GRID, true, false, false, 1>),
+                         dim3((unsigned)p.rows), dim3(NT), 0, s, a);
     return hip_fail(hipGetLastError(), "dense attention launch");
   }
   return p.nB > kColChunk ? launch_sparse<D, BLK, true>(p, a, flags, s)
