@@ -361,6 +361,64 @@ def test_sparse_attention_matches_oracle(entry):
         assert torch.equal(outs[fl].view(torch.int16), outs[F.FVA_SCHED_QUEUE].view(torch.int16))
 
 
+def _cu_count():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+@pytest.mark.parametrize("d,blk", [(128, 128), (128, 64), (64, 128), (64, 64)])
+@pytest.mark.parametrize("many", [False, True], ids=["teams", "one-team"])
+def test_both_kernel_families_match_oracle(d, blk, many):
+    # launches with no more rows than CUs run each row with several teams of
+    # waves (merged softmax states); larger ones run one team per row.  Both
+    # families, for every (d, block) pair, against the oracle, with every
+    # schedule giving the same bits and the dense kernel at p = 1 too.
+    block = (1, 8, 8) if blk == 64 else (1, 8, 16)
+    grid = (2, 40, 48) if blk == 64 else (4, 40, 48)     # 60 blocks per head, last one full
+    heads = (_cu_count() + 59) // 60 + 1 if many else 2
+    w = small_workload(f"family-d{d}-b{blk}", heads, d, grid, block, 0.85, 3,
+                       amp=tuple(0.5 + 0.3 * h for h in range(heads)))
+    assert (w.Hh * w.nB > _cu_count()) == many
+    q, k, v, qd, kd, vd, buf = setup(w)
+    gpu_reorder(buf, qd, kd, vd)
+    qr = O.reorder(q.float().numpy(), w.grid, w.block)
+    kr = O.reorder(k.float().numpy(), w.grid, w.block)
+    vr = O.reorder(v.float().numpy(), w.grid, w.block)
+    r = O.route_path(qr, kr, w.N, w.BLK, w.scale, w.top_p, w.topk_floor, w.aug_budget)
+    route(buf, w, scores_in=r["scores32"])
+    check_mask_exact(buf, r, w.nB)
+    rng = np.random.default_rng(11)
+    rows = sorted(set(rng.choice(w.Hh * w.nB, size=12, replace=False).tolist())
+                  | {int(np.argmax(r["counts"].reshape(-1)))})
+    items = [(row // (w.Hh * w.nB), (row // w.nB) % w.Hh, row % w.nB) for row in rows]
+    ref = O.sparse_attention(qr, kr, vr, r["mask"], w.N, w.BLK, w.scale, items=items)
+    outs = {}
+    for fl in (F.FVA_SCHED_QUEUE, F.FVA_SCHED_STATIC, F.FVA_SCHED_GRID, F.FVA_SCHED_XCD):
+        buf.orr.fill_(float("nan"))
+        attn(buf, fl)
+        torch.cuda.synchronize()
+        outs[fl] = buf.orr.clone()
+    for fl in (F.FVA_SCHED_STATIC, F.FVA_SCHED_GRID, F.FVA_SCHED_XCD):
+        assert torch.equal(outs[fl].view(torch.int16), outs[F.FVA_SCHED_QUEUE].view(torch.int16))
+    got_all = to_np(outs[F.FVA_SCHED_QUEUE])
+    assert np.all(np.isfinite(got_all[:, :, :w.N]))
+    num = den = mx = 0.0
+    for (b, h, i), o_ref in ref.items():
+        got = got_all[b, h, i * w.BLK:i * w.BLK + o_ref.shape[0]]
+        diff = np.abs(got - o_ref)
+        mx = max(mx, float(diff.max()))
+        num += float(diff.sum())
+        den += float(np.abs(o_ref).sum())
+    assert mx <= MAX_ABS and num / den <= MEAN_REL, (mx, num / den)
+    # p = 1 selects every block: the sparse kernel equals the dense one bit for bit
+    route(buf, w, top_p=1.0)
+    buf.orr.fill_(float("nan"))
+    attn(buf, F.FVA_SCHED_XCD)
+    dense = torch.full_like(buf.orr, float("nan"))
+    F.fva_dense_attn(buf.qr, buf.kr, buf.vt, dense, w.B, w.Hh, w.d, buf.grid)
+    torch.cuda.synchronize()
+    assert torch.equal(dense.view(torch.int16), buf.orr.view(torch.int16))
+
+
 @pytest.mark.parametrize("entry", SMALL, ids=[e[0] for e in SMALL])
 def test_dense_attention_matches_oracle_and_full_mask(entry):
     w = _wl(entry)
