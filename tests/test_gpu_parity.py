@@ -177,6 +177,17 @@ def test_reorder_strided_source():
     torch.cuda.synchronize()
     ref = O.reorder(qv.contiguous().view(torch.int16).numpy(), w.grid, w.block)
     assert np.array_equal(bits(buf.qr), ref)
+    # the pooling reorders read the same strided view, for both layouts
+    means = O.pool(O.reorder(qv.float().numpy(), w.grid, w.block), w.N, w.BLK).reshape(-1, w.d)
+    for dst, lay in ((buf.qr, F.FVA_LAYOUT_ROWS), (buf.kr, F.FVA_LAYOUT_K64)):
+        dst.fill_(float("nan"))
+        buf.qbar.fill_(float("nan"))
+        F.fva_reorder_pool(qd, dst, buf.qbar, w.B, w.Hh, w.d, buf.grid, None, F.token_strides(qd),
+                           lay)
+        torch.cuda.synchronize()
+        want = ref if lay == F.FVA_LAYOUT_ROWS else k64_expected(ref)
+        assert np.array_equal(bits(dst), want)
+        assert np.abs(buf.qbar.cpu().numpy() - means).max() <= 1e-5 * max(1.0, float(np.abs(means).max()) * 4)
 
 
 # ----------------------------------------------------------------- routing
