@@ -245,7 +245,11 @@ fva_status fva_route_flags(const void* ws, uint32_t* flags_out, hipStream_t stre
  * softmax.  Rows with no selected block, and pad rows, are written as zero.
  * qr: `rows` bf16; kr: `k64` bf16; vt: `v64` bf16; out: `rows` bf16.
  * scale <= 0 selects 1/sqrt(d).  flags: one FVA_SCHED_* value, optionally
- * | FVA_TRACE.  ws: fva_sizes().attn_ws_bytes bytes, 256-byte aligned
+ * | FVA_TRACE.  The schedule changes where and when rows run, never their
+ * bits: every schedule computes each row the same way.  (A launch with no
+ * more rows than the device has CUs runs one workgroup per row under every
+ * schedule, with teams of waves sharing the row's key blocks; fva_dense_attn
+ * does the same for such problems.)  ws: fva_sizes().attn_ws_bytes bytes, 256-byte aligned
  * (scheduler counters and lists; contents need not be initialized).
  * trace (with FVA_TRACE): trace_bytes bytes; record k (8 x uint32) describes
  * the k-th processed queue entry: {row, XCC_ID, HW_ID, workgroup id,
