@@ -629,11 +629,20 @@ __global__ void topup_pick_kernel(TopupState* __restrict__ st, uint32_t* __restr
     if ((int64_t)h[d] >= nd) break;
     nd -= h[d];
   }
+  // when digit d's bucket holds exactly the pairs still needed, every key
+  // with this prefix is taken and the lower digits cannot change the set:
+  // the bound is the first key past the bucket (with distinct scores this
+  // ends the select after the four score digits)
+  const bool whole = d < 256 && (int64_t)h[d] == nd;
   for (int b = 0; b < 256; ++b) h[b] = 0u;
+  const int sh = pass == 7 ? 0 : 54 - 8 * pass;
   s.need = nd;
   s.prefix = (s.prefix << (pass == 7 ? 6 : 8)) | d;
+  if (pass == 7 || whole) {
+    thresh[bh] = (s.prefix + 1ull) << sh;
+    s.mode = 0;
+  }
   st[bh] = s;
-  if (pass == 7) thresh[bh] = s.prefix + 1ull;
 }
 
 // One workgroup per row of a topped-up head: add pairs below the threshold,
