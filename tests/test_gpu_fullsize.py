@@ -236,3 +236,34 @@ def test_route_of_the_widest_rows_sampled(top_p, topk):
     ci = col_idx[torch.from_numpy(sample).cuda()].cpu().numpy()
     for k in range(len(sample)):
         assert np.array_equal(ci[k, :counts[k]], np.nonzero(mask[k])[0])
+
+
+@pytest.mark.parametrize("name", ["720p", "hetero"])
+def test_per_cu_imbalance_target_at_full_size(name):
+    # the balance target on one GPU: under the XCD schedule the traced launch's
+    # per-CU load-imbalance factor (max over mean busy time over all CUs, the
+    # oracle's definition) is at most 1.10, and so is the per-slot factor;
+    # the fixed contiguous split is shown beside it for scale
+    w = WORKLOADS[name]
+    q, k, v = make_qkv(w)
+    buf = F.alloc_buffers(w.grid, w.block, w.B, w.Hh, w.d, trace=True)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    F.forward(buf, qd, kd, vd, w.top_p, w.topk_floor, w.aug_budget, attn_flags=F.FVA_SCHED_XCD)
+    torch.cuda.synchronize()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rows = int(buf.sizes.rows)
+    lam = {}
+    for fl in (F.FVA_SCHED_STATIC, F.FVA_SCHED_XCD):
+        buf.trace.zero_()
+        F.fva_sparse_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, buf.grid, buf.mask(),
+                          0.0, fl | F.FVA_TRACE, buf.attn_ws, buf.sizes.attn_ws_bytes, buf.trace)
+        torch.cuda.synchronize()
+        recs = buf.trace.cpu().numpy().view(np.uint32).reshape(-1, 8)[:rows].tolist()
+        assert sorted(r[0] for r in recs) == list(range(rows))      # every item traced once
+        slots = len({r[3] for r in recs})                           # resident workgroups used
+        lam[fl] = (O.cu_imbalance(recs, cus), O.slot_imbalance(recs, slots))
+    print(f"[{name}] lambda_cu static {lam[F.FVA_SCHED_STATIC][0]:.3f} -> XCD "
+          f"{lam[F.FVA_SCHED_XCD][0]:.3f}; lambda_slot {lam[F.FVA_SCHED_STATIC][1]:.3f} -> "
+          f"{lam[F.FVA_SCHED_XCD][1]:.3f}", flush=True)
+    assert lam[F.FVA_SCHED_XCD][0] <= 1.10
+    assert lam[F.FVA_SCHED_XCD][1] <= 1.10
