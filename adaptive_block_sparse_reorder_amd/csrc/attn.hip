@@ -49,7 +49,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int KT = 64;           // keys per sub-tile
 constexpr int kColChunk = 2048;  // column-list entries staged in LDS at a time
-constexpr int NXCD = 8;          // XCDs; workgroup b is dispatched to XCD b % 8
+constexpr int NXCD = 8;          // XCDs; workgroups are dealt to them round robin
 constexpr float kLazy = 8.0f;    // log2-domain slack before the reference max moves
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -111,6 +111,7 @@ struct AttnArgs {
   int64_t rows;
   int nB;
   float sl2;   // scale * log2(e)
+  float isl2;  // 1 / sl2: the lazy threshold is kept in raw-score units
   int direct;  // 1: queue entry i is row i (every item is resident at once, so
                // the order of the queue buys nothing and its read is skipped)
 };
@@ -165,7 +166,11 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK) * TEAMS) __attribute__((amdgp
   // the wave adds k*NW*1024 (each wave instruction moves 1 KB contiguously)
   const uint32_t loff = (uint32_t)(wave * 64 + lane) * 16u;
 
-  const int xcd = blockIdx.x % NXCD;
+  // the XCD this workgroup runs on, read from the hardware (XCC_ID): the
+  // dispatcher deals workgroups round robin over the XCDs, but the XCD of
+  // workgroup 0 is not fixed (it moved when other queues had work), and the
+  // lists only pay off when the XCD that takes a list is the one it runs on
+  const int xcd = (int)(__builtin_amdgcn_s_getreg((31 << 11) | 20) & (NXCD - 1));
   int victim = 0;  // XCD schedule: how far thread 0 has moved from its own XCD
 
   // fetch the next item (position in the schedule's row list); -1 when done
@@ -202,7 +207,9 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK) * TEAMS) __attribute__((amdgp
   } else if (SCHED == FVA_SCHED_QUEUE || SCHED == FVA_SCHED_XCD) {
     item = fetch();
   } else if (DENSE) {
-    // XCD-aware remap: XCD x walks a contiguous range of rows (whole heads)
+    // XCD-aware remap: the workgroups b with one residue b mod 8 share an XCD
+    // (round-robin dealing), so each XCD walks a contiguous range of rows
+    // (whole heads); a bijection of b whichever XCD the dealing starts on
     const int64_t b = blockIdx.x;
     item = (a.rows % NXCD == 0) ? (b % NXCD) * (a.rows / NXCD) + b / NXCD : b;
   } else {
@@ -280,9 +287,11 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK) * TEAMS) __attribute__((amdgp
       for (int j = 0; j < QT; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][j][r] = 0.f;
-    float m_use[QT], l_run[QT];
+    // m_use: reference max (log2 domain); m_thr: the raw score above which a
+    // tile moves it, (m_use + kLazy) / sl2, so a tile's test is one compare
+    float m_use[QT], l_run[QT], m_thr[QT];
 #pragma unroll
-    for (int j = 0; j < QT; ++j) { m_use[j] = -INFINITY; l_run[j] = 0.f; }
+    for (int j = 0; j < QT; ++j) { m_use[j] = -INFINITY; l_run[j] = 0.f; m_thr[j] = -INFINITY; }
 
     // S^T of sub-tile u: keys 32m + (acc row) x queries 32j + l32
     auto qk = [&](int u, f32x16 (&s)[2][QT]) {
@@ -328,14 +337,14 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK) * TEAMS) __attribute__((amdgp
           for (int r = (m == 0 ? 2 : 0); r < 16; ++r) v = fmaxf(v, s[m][j][r]);
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
                                                          false, false);
-        mx[j] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.sl2;
-        grow = grow || (mx[j] > m_use[j] + kLazy);
+        mx[j] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        grow = grow || (mx[j] > m_thr[j]);
       }
       // move the reference max only when a tile exceeds it by 2^8
       if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
         for (int j = 0; j < QT; ++j) {
-          const float m_new = fmaxf(m_use[j], mx[j]);
+          const float m_new = fmaxf(m_use[j], mx[j] * a.sl2);
           const float alpha = __builtin_amdgcn_exp2f(m_use[j] - m_new);
           l_run[j] *= alpha;
 #pragma unroll
@@ -343,6 +352,7 @@ __global__ __launch_bounds__(attn_threads<QT>(BLK) * TEAMS) __attribute__((amdgp
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[dt][j][r] *= alpha;
           m_use[j] = m_new;
+          m_thr[j] = (m_new + kLazy) * a.isl2;
         }
       }
     };
@@ -739,6 +749,7 @@ fva_status launch_attn(const Problem& p, const void* qr, const void* kr, const v
   a.rows = p.rows;
   a.nB = p.nB;
   a.sl2 = scale * 1.4426950408889634f;
+  a.isl2 = 1.0f / a.sl2;
   a.direct = 0;
   if (p.d == 128 && p.BLK == 128) return launch_t<128, 128>(p, a, flags, dense, s);
   if (p.d == 128 && p.BLK == 64) return launch_t<128, 64>(p, a, flags, dense, s);

@@ -955,8 +955,10 @@ def test_persistent_multi_item_all_rows_every_schedule():
 
 def test_lambda_cu_matches_oracle_and_xcd_dispatch():
     # bench's per-CU and per-slot imbalance on real traces equal the oracle's
-    # definition; and workgroup b runs on XCD b mod 8, which the XCD schedule
-    # assumes
+    # definition; workgroups are dealt to the XCDs round robin (all b with one
+    # residue mod 8 on one XCD: the dense remap's locality premise), and the
+    # XCD schedule, which picks its list by the XCD it reads from the
+    # hardware, runs each head's rows on one XCD
     import bench
     w = _multi_item_workload()
     q, k, v, qd, kd, vd, buf = setup(w)
@@ -979,10 +981,20 @@ def test_lambda_cu_matches_oracle_and_xcd_dispatch():
         assert got["lambda_slot"] == pytest.approx(want_slot, rel=1e-12)
         assert got["cus"] == len(O.trace_unit_busy(recs)) <= cus
         tr = np.array(recs, dtype=np.uint32)
-        xcc = tr[:, 1] & 0xF
-        mismatch = int((xcc != tr[:, 3] % 8).sum())
-        print(f"sched {fl}: {mismatch} of {len(recs)} items off XCD (workgroup id mod 8)")
-        assert mismatch == 0
+        xcc = (tr[:, 1] & 0xF).astype(np.int64)
+        res = (tr[:, 3] % 8).astype(np.int64)
+        first = sorted({int(x - r) % 8 for x, r in zip(xcc, res)})
+        print(f"sched {fl}: workgroup b ran on XCD (b + c) mod 8 for c in {first}")
+        for r in range(8):
+            assert len(set(xcc[res == r].tolist())) <= 1, (fl, r)
+        if fl == F.FVA_SCHED_XCD:
+            head = tr[:, 0].astype(np.int64) // int(buf.sizes.nB)
+            on = sum(int(np.bincount(xcc[head == h]).max()) for h in np.unique(head))
+            print(f"sched {fl}: {on} of {len(recs)} rows on their head's XCD")
+            # each of the 8 heads has a list of 102 rows to itself; the first 64
+            # rows of a list go to its own XCD's 64 workgroups before any XCD
+            # can run dry and steal, so at least 512 of 816 rows run there
+            assert on >= 0.6 * len(recs)
 
 
 def test_forward_replays_under_hip_graph_capture():
