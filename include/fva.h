@@ -243,6 +243,8 @@ fva_status fva_route_flags(const void* ws, uint32_t* flags_out, hipStream_t stre
  *         softmax_k((q . k) * scale) * v_k,
  * computed with bf16 MFMA products, float32 accumulation and an online
  * softmax.  Rows with no selected block, and pad rows, are written as zero.
+ * Inputs must be finite: the kernels are compiled without NaN semantics, so
+ * a NaN or infinity in Q, K or V gives an unspecified result for its rows.
  * qr: `rows` bf16; kr: `k64` bf16; vt: `v64` bf16; out: `rows` bf16.
  * scale <= 0 selects 1/sqrt(d).  flags: one FVA_SCHED_* value, optionally
  * | FVA_TRACE.  The schedule changes where and when rows run, never their
