@@ -9,6 +9,8 @@ For every full workload:
   * attention output on a sample of query blocks (heaviest, lightest, the
     ragged last block of a head, seeded random ones) is within max-abs 2e-2
     and mean-relative 5e-3 of the oracle, computed block by block;
+  * the dense comparator's output on the same blocks is within the same bounds
+    of the oracle with every block selected;
   * on the same blocks the sparse and dense per-query log-sum-exp are within
     5e-3 of the oracle and the mask recall exp(lse_sparse - lse_dense) within
     1e-2 (bf16-rounded probabilities are summed, each within 2^-9 relative).
@@ -148,9 +150,25 @@ def run_case(w, n_random=12):
           flush=True)
     assert mx <= MAX_ABS and num / den <= MEAN_REL
 
-    print(f"[{w.name}] log-sum-exp and recall on the same blocks", flush=True)
+    print(f"[{w.name}] dense comparator, log-sum-exp and recall on the same blocks", flush=True)
+    buf.orr.fill_(float("nan"))
     F.fva_dense_attn(buf.qr, buf.kr, buf.vt, buf.orr, w.B, w.Hh, w.d, buf.grid, lse=lse_d)
     torch.cuda.synchronize()
+    # the dense output on the sampled blocks against the oracle with every
+    # block selected
+    ref_dense = O.sparse_attention(qr, kr, vr, np.ones_like(r["mask"]), w.N, w.BLK, w.scale,
+                                   items=items)
+    num = den = mx = 0.0
+    for (b, h, i), o_ref in ref_dense.items():
+        lo = i * w.BLK
+        got = buf.orr[b, h, lo:lo + o_ref.shape[0]].float().cpu().numpy()
+        diff = np.abs(got - o_ref)
+        mx = max(mx, float(diff.max()))
+        num += float(diff.sum())
+        den += float(np.abs(o_ref).sum())
+    print(f"[{w.name}] dense {len(items)} blocks: max_abs={mx:.3e} mean_rel={num / den:.3e}",
+          flush=True)
+    assert mx <= MAX_ABS and num / den <= MEAN_REL
     gs = lse_s.cpu().numpy().astype(np.float64).reshape(w.B, w.Hh, w.N)
     gd = lse_d.cpu().numpy().astype(np.float64).reshape(w.B, w.Hh, w.N)
     full_row = np.ones(w.nB, dtype=bool)
